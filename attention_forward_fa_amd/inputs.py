@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for the fused attention forward pass.
+
+This module holds none of the attention arithmetic. It draws Q, K and V,
+rounds them to their storage type and, for fp8, quantizes every
+(batch, head) slice with its own amax/448 scale. The HIP path and the CPU
+oracle both consume exactly the bytes produced here, so neither side ever
+sees a value the other did not.
+
+Recipe (the workloads of the five attention configurations):
+  * Q, K, V drawn in that order as iid N(0, 1) float32 of shape [B, H, N, d]
+    from ``torch.Generator('cpu').manual_seed(seed)``;
+  * fp16 / bf16: round-to-nearest-even cast of the float32 draw;
+  * fp8 (OCP e4m3fn): per (b, h) slice, ``amax = max |x|`` over N x d,
+    ``s = amax / 448`` in float32 (``s = 1`` for an all-zero slice), codes =
+    RNE(clamp(x / s, -448, 448)); ``s`` is the dequantization scale
+    ("descale") handed to both sides.
+  * scale = 1/sqrt(d) rounded to float32, unless the caller fixes another.
+
+Arrays are returned as raw storage bits (uint16 for fp16/bf16, uint8 for fp8)
+so that no float conversion can happen silently on either side.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+DTYPES = ("fp16", "bf16", "fp8")
+FP8_MAX = 448.0  # largest finite OCP e4m3fn magnitude
+
+_TORCH_STORAGE = {
+    "fp16": torch.float16,
+    "bf16": torch.bfloat16,
+    "fp8": torch.float8_e4m3fn,
+}
+_BITS_VIEW = {"fp16": torch.int16, "bf16": torch.int16, "fp8": torch.uint8}
+_NP_BITS = {"fp16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
+
+
+@dataclasses.dataclass
+class AttnInputs:
+    """One attention problem: storage bits of Q, K, V plus its parameters."""
+
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: float  # a float32 value
+    q: np.ndarray  # [B, H, N, d] storage bits
+    k: np.ndarray
+    v: np.ndarray
+    descale_q: Optional[np.ndarray] = None  # [B*H] float32, fp8 only
+    descale_k: Optional[np.ndarray] = None
+    descale_v: Optional[np.ndarray] = None
+    seed: Optional[int] = None
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+    def describe(self) -> str:
+        return (f"B={self.B} H={self.H} N={self.N} d={self.d} dtype={self.dtype} "
+                f"causal={int(self.causal)} seed={self.seed}")
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to float32."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _bits(t: torch.Tensor, dtype: str) -> np.ndarray:
+    return t.contiguous().view(_BITS_VIEW[dtype]).numpy().view(_NP_BITS[dtype]).copy()
+
+
+def _quantize_fp8(x: torch.Tensor):
+    """Per-(b, h) amax/448 quantization to e4m3fn; returns (codes, descale[B*H])."""
+    B, H = x.shape[0], x.shape[1]
+    amax = x.abs().amax(dim=(2, 3)).to(torch.float32)
+    s = amax / torch.tensor(FP8_MAX, dtype=torch.float32)
+    s = torch.where(amax > 0, s, torch.ones_like(s))
+    y = (x / s[:, :, None, None]).clamp(-FP8_MAX, FP8_MAX)
+    codes = y.to(torch.float8_e4m3fn)
+    return _bits(codes, "fp8"), s.reshape(B * H).numpy().astype(np.float32)
+
+
+def from_float(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dtype: str,
+               causal: bool = False, scale: Optional[float] = None,
+               seed: Optional[int] = None) -> AttnInputs:
+    """Round float32 tensors [B, H, N, d] to the storage type (RNE; fp8 quantized)."""
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
+    q, k, v = (t.detach().to("cpu", torch.float32).contiguous() for t in (q, k, v))
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+    if dtype == "fp8":
+        (qb, dq), (kb, dk), (vb, dv) = (_quantize_fp8(t) for t in (q, k, v))
+        return AttnInputs(B, H, N, d, dtype, bool(causal), scale, qb, kb, vb,
+                          dq, dk, dv, seed)
+    st = _TORCH_STORAGE[dtype]
+    qb, kb, vb = (_bits(t.to(st), dtype) for t in (q, k, v))
+    return AttnInputs(B, H, N, d, dtype, bool(causal), scale, qb, kb, vb, seed=seed)
+
+
+def draw(B: int, H: int, N: int, d: int, dtype: str, causal: bool, seed: int,
+         scale: Optional[float] = None) -> AttnInputs:
+    """The seeded iid N(0, 1) workload of the recipe above."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    return from_float(q, k, v, dtype, causal, scale, seed)
+
+
+# The five workloads: (name, B, H, N, d, dtype, causal, seed).  The first is the
+# small case the oracle finishes in well under a second; the third is the
+# d=128, N=4096 fp16 roofline workload.
+CONFIGS = (
+    ("fp16_b1h2_n256_d64", 1, 2, 256, 64, "fp16", False, 1),
+    ("fp16_b4h16_n1024_d64", 4, 16, 1024, 64, "fp16", False, 2),
+    ("fp16_b2h16_n4096_d128", 2, 16, 4096, 128, "fp16", False, 3),
+    ("bf16_causal_b1h32_n8192_d128", 1, 32, 8192, 128, "bf16", True, 4),
+    ("fp8_causal_b1h32_n16384_d128", 1, 32, 16384, 128, "fp8", True, 5),
+)
+
+
+def config(name_or_index) -> tuple:
+    if isinstance(name_or_index, int):
+        return CONFIGS[name_or_index]
+    for c in CONFIGS:
+        if c[0] == name_or_index:
+            return c
+    raise KeyError(name_or_index)
+
+
+def draw_config(name_or_index) -> AttnInputs:
+    _, B, H, N, d, dtype, causal, seed = config(name_or_index)
+    return draw(B, H, N, d, dtype, causal, seed)
