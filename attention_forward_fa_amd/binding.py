@@ -1,0 +1,188 @@
+"""Thin ctypes binding of libfa_mi355x.so (include/fa_mi355x.h).
+
+Argument marshalling only: every step of the attention forward pass runs in
+the library's HIP kernels.  torch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or refuses the call,
+an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+from .build import LIB_PATH
+
+FA_DTYPE_FP16 = 0
+FA_DTYPE_BF16 = 1
+FA_DTYPE_FP8_E4M3 = 2
+_TORCH_DTYPE_CODE = {
+    torch.float16: FA_DTYPE_FP16,
+    torch.bfloat16: FA_DTYPE_BF16,
+    torch.float8_e4m3fn: FA_DTYPE_FP8_E4M3,
+}
+
+# Exported symbols, with their C signatures.
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+SIGNATURES = {
+    "fa_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float,
+                              ctypes.c_int, ctypes.c_int, _P]),
+    "fa_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                                  ctypes.c_float, ctypes.c_int, _P]),
+    "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fa_abi_version": (ctypes.c_int, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa_mi355x status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: Optional[str] = None):
+    """Load libfa_mi355x.so (built in-tree by attention_forward_fa_amd.build)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise FileNotFoundError(
+                f"{p} is missing: build it first (python -m attention_forward_fa_amd.build)")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise FAError(status, status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _validate(q, k, v):
+    if not (isinstance(q, torch.Tensor) and isinstance(k, torch.Tensor)
+            and isinstance(v, torch.Tensor)):
+        raise TypeError("q, k, v must be torch tensors")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _TORCH_DTYPE_CODE:
+        raise TypeError("q, k, v must all be float16, bfloat16 or float8_e4m3fn")
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise ValueError("q, k, v must be device tensors")
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [B, H, N, d]")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+
+
+def _outputs(q, out, lse):
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != (B, H, N, d) or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 [B, H, N, d] tensor")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    return out, lse
+
+
+def _default_scale(d: int) -> float:
+    return float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O (fp16) and LSE (fp32) of softmax(scale Q K^T [+ causal mask]) V.
+
+    fp8 (float8_e4m3fn) inputs are taken at unit scale; see ``fwd_fp8``.
+    Runs on the current stream of q's device.
+    """
+    _validate(q, k, v)
+    B, H, N, d = q.shape
+    out, lse = _outputs(q, out, lse)
+    scale = _default_scale(d) if scale is None else float(scale)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                        int(bool(causal)), _TORCH_DTYPE_CODE[q.dtype], stream)
+    _check(st)
+    return out, lse
+
+
+def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, descale_q: torch.Tensor,
+            descale_k: torch.Tensor, descale_v: torch.Tensor, causal: bool = False,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fp8 e4m3 attention with per-head dequantization scales (float32 [B*H])."""
+    _validate(q, k, v)
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError("fwd_fp8 takes float8_e4m3fn q, k, v")
+    B, H, N, d = q.shape
+    for t in (descale_q, descale_k, descale_v):
+        if (t.dtype != torch.float32 or t.numel() != B * H or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError("descales must be contiguous float32 device tensors of B*H values")
+    out, lse = _outputs(q, out, lse)
+    scale = _default_scale(d) if scale is None else float(scale)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(descale_q), _ptr(descale_k),
+                            _ptr(descale_v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                            int(bool(causal)), stream)
+    _check(st)
+    return out, lse
+
+
+# Storage dtype names of the input generator -> torch dtypes.
+TORCH_DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+
+
+def to_device(inp, device="cuda"):
+    """Upload an input set's storage bits as torch tensors (no conversion)."""
+    import numpy as np
+
+    def up(bits):
+        raw = np.ascontiguousarray(bits)
+        raw = raw.view(np.uint8) if inp.dtype == "fp8" else raw.view(np.int16)
+        return torch.from_numpy(raw).to(device).view(TORCH_DTYPES[inp.dtype])
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    ds = None
+    if inp.dtype == "fp8":
+        ds = tuple(torch.from_numpy(x).to(device) for x in
+                   (inp.descale_q, inp.descale_k, inp.descale_v))
+    return q, k, v, ds
+
+
+def run_inputs(inp, device="cuda", out=None, lse=None):
+    """Run the library on an input set (fp8 with its per-head descales)."""
+    q, k, v, ds = to_device(inp, device)
+    if inp.dtype == "fp8":
+        return fwd_fp8(q, k, v, *ds, causal=inp.causal, scale=inp.scale, out=out, lse=lse)
+    return fwd(q, k, v, causal=inp.causal, scale=inp.scale, out=out, lse=lse)

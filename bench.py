@@ -1,0 +1,164 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward pass on one MI355X.
+
+A step is one fa_fwd call over the whole workload (all of B x H x N query
+rows), inputs already resident in device memory.  Default workload: fp16,
+non-causal, B=2, H=16, N=4096, d=128 (the d=128 roofline workload).
+
+Prints one JSON line:
+  value     counted TFLOPS = 4*B*H*N^2*d (halved if causal) / time per step
+  roofline  the kernel against the MI355X dense MFMA peak of its input type,
+            timed with HIP events on the stream the kernel is launched on
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS (4BHN²d/t) and % of MI355X MFMA peak, 1 GPU"
+DEFAULT_WORKLOAD = "fp16_b2h16_n4096_d128"
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="workload name (attention_forward_fa_amd.inputs.CONFIGS)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every workload and print one line each to stderr")
+    return ap.parse_args(argv)
+
+
+def time_gpu(inp, steps, warmup):
+    """Average seconds per fa_fwd call, HIP events on the launch stream."""
+    import torch
+
+    from attention_forward_fa_amd import binding
+
+    q, k, v, ds = binding.to_device(inp, "cuda")
+    out = torch.empty((inp.B, inp.H, inp.N, inp.d), dtype=torch.float16, device="cuda")
+    lse = torch.empty((inp.B, inp.H, inp.N), dtype=torch.float32, device="cuda")
+
+    def step():
+        if inp.dtype == "fp8":
+            binding.fwd_fp8(q, k, v, *ds, causal=inp.causal, scale=inp.scale, out=out, lse=lse)
+        else:
+            binding.fwd(q, k, v, causal=inp.causal, scale=inp.scale, out=out, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / steps
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle, as it stands, on whole heads of the workload until the budget runs out."""
+    import threadpoolctl
+
+    from attention_forward_fa_amd import accounting
+    from oracle import attention as oracle
+
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    BH = inp.B * inp.H
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < BH:
+        oracle.run(inp, heads=[heads])
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = accounting.counted_flops(1, heads, inp.N, inp.d, inp.causal)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{heads} of {BH} heads, all {inp.N} query rows each, "
+                      f"fp64 numpy/BLAS, {dt:.1f} s"}
+
+
+def describe(inp, sec):
+    from attention_forward_fa_amd import accounting as acc
+
+    flops = acc.counted_flops(inp.B, inp.H, inp.N, inp.d, inp.causal)
+    tf = flops / sec / 1e12
+    peak = acc.PEAK_TFLOPS[inp.dtype]
+    return flops, tf, peak
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention "
+              "forward pass here runs on a single device and has no multi-GPU path",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    from attention_forward_fa_amd import accounting as acc
+    from attention_forward_fa_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    name, B, H, N, d, dtype, causal, seed = inputs.config(args.workload)
+    inp = inputs.draw(B, H, N, d, dtype, causal, seed)
+    sec = time_gpu(inp, args.steps, args.warmup)
+    flops, tf, peak = describe(inp, sec)
+    if args.sweep:
+        for cfg in inputs.CONFIGS:
+            x = inputs.draw(*cfg[1:8])
+            s = time_gpu(x, max(10, args.steps // 4), args.warmup)
+            _, t, pk = describe(x, s)
+            print(json.dumps({"workload": cfg[0], "ms": round(s * 1e3, 4),
+                              "tflops": round(t, 2), "frac": round(t / pk, 4)}),
+                  file=sys.stderr, flush=True)
+    rec = {
+        "metric": METRIC,
+        "value": round(tf, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp16": "f16", "bf16": "bf16", "fp8": "fp8e4m3"}[dtype],
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "H": H, "N": N, "d": d,
+                   "input_dtype": dtype, "causal": bool(causal), "seed": seed,
+                   "outputs": "O fp16 + LSE fp32", "accumulate": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None},
+        "frac_of_peak": round(tf / peak, 4),
+        "algorithmic_bytes": acc.algorithmic_bytes(B, H, N, d, dtype),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

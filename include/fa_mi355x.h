@@ -1,0 +1,109 @@
+/*
+ * fa_mi355x.h -- C ABI of the fused attention forward library for AMD
+ * Instinct MI355X (gfx950).  Library: libfa_mi355x.so.
+ *
+ * Operation.  For every batch b and head h, with Q, K, V the [N, d] slices:
+ *
+ *     S   = scale * Q K^T                 (fp32 accumulation)
+ *     S_ij = -inf  where causal and j > i  (key j is kept iff j <= query i)
+ *     O   = softmax_rows(S) V             (stored as fp16)
+ *     LSE_i = ln sum_j exp(S_ij)          (fp32, natural log)
+ *
+ * computed as a fused pass that tiles the queries, streams K/V blocks through
+ * on-chip memory and keeps a running row max and row sum, so the N x N score
+ * matrix never reaches device memory.  The method is the one described in
+ * "TCA 51%，MFU 不足 8%——GPU 的隐藏性能损耗" (section "FA2 TCA 虚高归因":
+ * online softmax accumulates softmax@V block by block without materialising
+ * the [B, L, L] map) and in "第 17 章 TMA + Warp Specialization 把 FA2 写到
+ * SOTA" §17.5 (per K/V tile: S = Q K^T, running max/sum update, rescale of
+ * the O accumulator, O += P V, final division by the row sum).  The tensor
+ * layout [B, H, N, d] with d contiguous is the one of §17.3 of the same
+ * chapter.  The causal mask, the scale and the LSE output are not on those
+ * pages; they are defined as above.
+ *
+ * Conventions shared by every entry point:
+ *   - q, k, v, o, lse and the descale arrays are DEVICE pointers owned by the
+ *     caller; the library allocates, frees and retains nothing, keeps no
+ *     global state and may be called from several host threads at once.
+ *   - q, k, v: [B, H, N, d] contiguous, element type given by the dtype.
+ *     o: [B, H, N, d] contiguous IEEE fp16 for every input dtype.
+ *     lse: [B, H, N] contiguous fp32; required (never NULL when B*H*N > 0).
+ *     q, k, v, o must be 16-byte aligned, lse 4-byte aligned.
+ *   - d must be 64 or 128.  N >= 1 may be any length (ragged tails are
+ *     masked).  B, H >= 1.  If B*H*N == 0 the call does nothing and returns
+ *     FA_OK without reading any pointer.
+ *   - scale must be finite and > 0 (1/sqrt(d) is the usual choice).
+ *   - stream: a hipStream_t (NULL = the null stream).  The call only enqueues
+ *     work and returns; results are ready when the stream reaches that point.
+ *   - Errors: invalid arguments return a negative fa_status synchronously,
+ *     before any HIP runtime call, and nothing is launched.  A failed kernel
+ *     launch returns FA_ERR_LAUNCH.  Faults during execution surface at the
+ *     caller's next synchronisation with the stream, as usual for HIP.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_DTYPE_FP16 = 0,      /* IEEE binary16 */
+  FA_DTYPE_BF16 = 1,      /* bfloat16 */
+  FA_DTYPE_FP8_E4M3 = 2   /* OCP 8-bit E4M3 ("e4m3fn": no inf, max 448) */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,       /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,      /* B, H or N negative, or the problem is too large */
+  FA_ERR_HEAD_DIM = -3,   /* d not in {64, 128} */
+  FA_ERR_DTYPE = -4,      /* unknown dtype */
+  FA_ERR_ALIGN = -5,      /* a pointer is not aligned as required */
+  FA_ERR_LAUNCH = -6,     /* the HIP runtime refused the kernel launch */
+  FA_ERR_SCALE = -7,      /* scale not finite and positive */
+  FA_ERR_CAUSAL = -8      /* causal not 0 or 1 */
+} fa_status;
+
+/*
+ * fa_fwd -- attention forward for fp16, bf16 or fp8 inputs.
+ * With dtype FA_DTYPE_FP8_E4M3 every head uses unit dequantization scales
+ * (the fp8 codes are the values); use fa_fwd_fp8 to pass per-head scales.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+           int dtype, void* stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward for OCP e4m3 inputs with per-head
+ * dequantization scales.  The value of an input element is its e4m3 code
+ * value times the float32 scale of its (b, h) head: descale_q[b*H + h] for Q,
+ * and likewise for K and V.  descale_q, descale_k, descale_v are device
+ * arrays of B*H floats, each finite and > 0 (other values give unspecified
+ * results; they are not read on the host).  O and LSE are those of the
+ * dequantized problem.  QK^T runs on fp8 matrix instructions with fp32
+ * accumulation; P V runs in fp16 (the e4m3 values of V are exact in fp16).
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v,
+               const float* descale_q, const float* descale_k,
+               const float* descale_v, void* o, float* lse,
+               int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+               int causal, void* stream);
+
+/* Short English description of a status code (never NULL, static storage). */
+const char* fa_status_string(int status);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

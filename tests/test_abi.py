@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports what include/fa_mi355x.h declares and rejects
+invalid arguments before any HIP call (nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_forward_fa_amd import binding
+from attention_forward_fa_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH),
+                                reason="library not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(fa_[a-z0-9_]+)\s*\(",
+                      text, flags=re.M)
+
+
+def _header_constants():
+    text = open(HEADER, encoding="utf-8").read()
+    consts = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(FA_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+    consts["FA_ABI_VERSION"] = int(re.search(r"#define FA_ABI_VERSION (\d+)", text).group(1))
+    return consts
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert set(names) >= {"fa_fwd", "fa_fwd_fp8", "fa_status_string", "fa_abi_version"}
+    lib = ctypes.CDLL(LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    lib = binding.load_library()
+    c = _header_constants()
+    assert lib.fa_abi_version() == c["FA_ABI_VERSION"]
+    for name, val in c.items():
+        if name.startswith("FA_ERR_") or name == "FA_OK":
+            s = binding.status_string(val)
+            assert s and s != "unknown status", name
+    assert binding.status_string(12345) == "unknown status"
+
+
+# Fake, 16-byte aligned "device" addresses: never dereferenced, because every
+# call below fails validation (or is empty) before reaching the HIP runtime.
+A = 0x7F0000000000
+Q, K, V, O, L = A, A + 0x1000, A + 0x2000, A + 0x3000, A + 0x4000
+
+
+def _call(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=256, d=64, scale=0.125, causal=0,
+                dtype=0, stream=None)
+    args.update(kw)
+    return lib.fa_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                      args["H"], args["N"], args["d"], args["scale"], args["causal"],
+                      args["dtype"], args["stream"])
+
+
+def _call_fp8(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, dq=A + 0x5000, dk=A + 0x6000, dv=A + 0x7000, o=O, lse=L,
+                B=1, H=2, N=256, d=128, scale=0.1, causal=1, stream=None)
+    args.update(kw)
+    return lib.fa_fwd_fp8(args["q"], args["k"], args["v"], args["dq"], args["dk"], args["dv"],
+                          args["o"], args["lse"], args["B"], args["H"], args["N"], args["d"],
+                          args["scale"], args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), "FA_ERR_NULL"),
+    (dict(lse=None), "FA_ERR_NULL"),
+    (dict(o=None), "FA_ERR_NULL"),
+    (dict(B=-1), "FA_ERR_SHAPE"),
+    (dict(N=-5), "FA_ERR_SHAPE"),
+    (dict(N=1 << 25), "FA_ERR_SHAPE"),
+    (dict(d=96), "FA_ERR_HEAD_DIM"),
+    (dict(d=0), "FA_ERR_HEAD_DIM"),
+    (dict(dtype=3), "FA_ERR_DTYPE"),
+    (dict(dtype=-1), "FA_ERR_DTYPE"),
+    (dict(q=Q + 8), "FA_ERR_ALIGN"),
+    (dict(o=O + 2), "FA_ERR_ALIGN"),
+    (dict(lse=L + 2), "FA_ERR_ALIGN"),
+    (dict(scale=0.0), "FA_ERR_SCALE"),
+    (dict(scale=-0.5), "FA_ERR_SCALE"),
+    (dict(scale=float("inf")), "FA_ERR_SCALE"),
+    (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(causal=2), "FA_ERR_CAUSAL"),
+])
+def test_fa_fwd_rejects(kw, status):
+    assert _call(**kw) == _header_constants()[status]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=None), "FA_ERR_NULL"),
+    (dict(dv=None), "FA_ERR_NULL"),
+    (dict(dk=A + 0x6002), "FA_ERR_ALIGN"),
+    (dict(d=32), "FA_ERR_HEAD_DIM"),
+    (dict(causal=-1), "FA_ERR_CAUSAL"),
+])
+def test_fa_fwd_fp8_rejects(kw, status):
+    assert _call_fp8(**kw) == _header_constants()[status]
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0),
+                                dict(N=0, q=None, k=None, v=None, o=None, lse=None)])
+def test_empty_problem_is_a_noop(kw):
+    # B*H*N == 0: nothing to compute, no pointer is read, no launch.
+    assert _call(**kw) == 0
+    assert _call_fp8(**kw) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        binding.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,224 @@
+"""HIP path (through the C ABI) against the CPU fp64 oracle, element by element.
+
+Bars (absolute, element-wise, O upcast to float64 against the oracle's exact O):
+  fp16 / bf16:  max|dO| <= 4e-3, mean|dO| <= 5e-4, max|dLSE| <= 1e-3
+  fp8 (e4m3):   max|dO| <= 3e-2, mean|dO| <= 3.75e-3, max|dLSE| <= 1e-3
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from attention_forward_fa_amd import binding, inputs
+from oracle import attention as oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp16": (4e-3, 5e-4, 1e-3), "bf16": (4e-3, 5e-4, 1e-3), "fp8": (3e-2, 3.75e-3, 1e-3)}
+
+
+def announce(msg):
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+def gpu_run(inp, out=None, lse=None):
+    announce(inp.describe())
+    o, l = binding.run_inputs(inp, device="cuda", out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def to_np(o, l, inp):
+    o = o.float().cpu().numpy().astype(np.float64).reshape(inp.B * inp.H, inp.N, inp.d)
+    l = l.cpu().numpy().astype(np.float64).reshape(inp.B * inp.H, inp.N)
+    return o, l
+
+
+def check(inp, o, l, heads=None, rows=None, tol=None):
+    o_ref, l_ref = oracle.run(inp, rows=rows, heads=heads)
+    hsel = np.arange(inp.B * inp.H) if heads is None else np.asarray(heads)
+    rsel = np.arange(inp.N) if rows is None else np.asarray(rows)
+    og = o[hsel][:, rsel]
+    lg = l[hsel][:, rsel]
+    assert np.isfinite(og).all() and np.isfinite(lg).all(), inp.describe()
+    mx_o, mean_o, mx_l = tol or TOL[inp.dtype]
+    d_o = np.abs(og - o_ref)
+    d_l = np.abs(lg - l_ref)
+    msg = (f"{inp.describe()}: max|dO|={d_o.max():.3e} mean|dO|={d_o.mean():.3e} "
+           f"max|dLSE|={d_l.max():.3e}")
+    announce(msg)
+    assert d_o.max() <= mx_o, msg
+    assert d_o.mean() <= mean_o, msg
+    assert d_l.max() <= mx_l, msg
+    return d_o.max(), d_o.mean(), d_l.max()
+
+
+# --- small shapes: whole outputs, several tiles and ragged tails -------------
+
+SMALL_N = (1, 17, 64, 100, 129, 300)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SMALL_N)
+def test_small_shapes(dtype, d, causal, N):
+    inp = inputs.draw(2, 3, N, d, dtype, causal, seed=1000 + N + d)
+    o, l = to_np(*gpu_run(inp), inp)
+    check(inp, o, l)
+
+
+def test_config1_full():
+    inp = inputs.draw_config(0)
+    o, l = to_np(*gpu_run(inp), inp)
+    check(inp, o, l)
+
+
+# --- the four large workloads at full size, oracle on sampled rows -----------
+
+def _sample_rows(N, seed, extra=24):
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, N // 2, N - 129, N - 128,
+             N - 65, N - 64, N - 2, N - 1]
+    rng = np.random.default_rng(seed)
+    rand = rng.integers(0, N, size=extra)
+    return np.unique(np.clip(np.concatenate([fixed, rand]), 0, N - 1))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_large_config_sampled(cfg):
+    inp = inputs.draw_config(cfg)
+    o, l = gpu_run(inp)
+    o, l = to_np(o, l, inp)
+    BH = inp.B * inp.H
+    heads = sorted({0, 1, BH // 2, BH - 1})
+    rows = _sample_rows(inp.N, seed=cfg)
+    check(inp, o, l, heads=heads, rows=rows)
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+# --- edge cases and closed forms -----------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_q_gives_mean_of_v(dtype, causal):
+    B, H, N, d = 1, 2, 200, 128
+    g = torch.Generator().manual_seed(21)
+    q = torch.zeros((B, H, N, d))
+    k = torch.randn((B, H, N, d), generator=g)
+    v = torch.randn((B, H, N, d), generator=g)
+    inp = inputs.from_float(q, k, v, dtype, causal)
+    o, l = to_np(*gpu_run(inp), inp)
+    check(inp, o, l)
+    expect = np.log(np.arange(1, N + 1)) if causal else np.full(N, np.log(N))
+    assert np.abs(l - expect[None, :]).max() <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
+def test_constant_v(dtype):
+    B, H, N, d = 1, 2, 150, 64
+    g = torch.Generator().manual_seed(22)
+    q = torch.randn((B, H, N, d), generator=g)
+    k = torch.randn((B, H, N, d), generator=g)
+    v = torch.full((B, H, N, d), 1.25)
+    inp = inputs.from_float(q, k, v, dtype, True)
+    o, l = to_np(*gpu_run(inp), inp)
+    check(inp, o, l)
+    assert np.abs(o - 1.25).max() <= 4e-3
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_row0_is_v0_exactly(dtype, d):
+    inp = inputs.draw(2, 2, 77, d, dtype, True, seed=23)
+    o, l = gpu_run(inp)
+    o_ref, _ = oracle.run(inp, rows=[0])
+    got = o.float().cpu().numpy().astype(np.float64).reshape(4, 77, d)[:, 0]
+    assert np.array_equal(got, o_ref[:, 0]), "causal row 0 must equal V[0] exactly"
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
+def test_large_scores(dtype):
+    # Scores of several hundred: the running max must be subtracted before exp.
+    inp = inputs.draw(1, 2, 130, 64, dtype, False, seed=24, scale=4.0)
+    o, l = to_np(*gpu_run(inp), inp)
+    tol = (TOL[dtype][0], TOL[dtype][1], 1e-3 * max(1.0, float(np.abs(l).max()) / 100))
+    check(inp, o, l, tol=tol)
+
+
+def test_fp8_unit_descale_entry_point():
+    # fa_fwd with dtype FP8 = codes taken at unit scale.
+    # Codes reach |448| at unit scale; a small softmax scale keeps scores moderate.
+    inp = inputs.draw(1, 2, 190, 128, "fp8", True, seed=25, scale=1e-4)
+    q, k, v, _ = binding.to_device(inp)
+    announce("fa_fwd fp8 unit descale " + inp.describe())
+    o, l = binding.fwd(q, k, v, causal=True, scale=inp.scale)
+    torch.cuda.synchronize()
+    unit = np.ones(inp.B * inp.H, dtype=np.float32)
+    ref_inp = inputs.AttnInputs(inp.B, inp.H, inp.N, inp.d, "fp8", True, inp.scale, inp.q,
+                                inp.k, inp.v, unit, unit, unit)
+    on, ln = to_np(o, l, inp)
+    # Unit-scale codes reach |v| = 448: the O bar scales with the value range.
+    check(ref_inp, on, ln, tol=(3e-2 * 448 / 4, 3.75e-3 * 448 / 4, 1e-3 * 30))
+
+
+def test_many_heads_distinct():
+    inp = inputs.draw(3, 5, 97, 64, "fp16", False, seed=26)
+    o, l = to_np(*gpu_run(inp), inp)
+    check(inp, o, l)
+
+
+def test_no_writes_outside_outputs():
+    inp = inputs.draw(1, 3, 131, 128, "bf16", True, seed=27)
+    n_o = inp.B * inp.H * inp.N * inp.d
+    n_l = inp.B * inp.H * inp.N
+    G = 4096
+    obuf = torch.full((n_o + 2 * G,), 7.0, dtype=torch.float16, device="cuda")
+    lbuf = torch.full((n_l + 2 * G,), 7.0, dtype=torch.float32, device="cuda")
+    out = obuf[G:G + n_o].view(inp.B, inp.H, inp.N, inp.d)
+    lse = lbuf[G:G + n_l].view(inp.B, inp.H, inp.N)
+    gpu_run(inp, out=out, lse=lse)
+    assert torch.all(obuf[:G] == 7.0) and torch.all(obuf[G + n_o:] == 7.0)
+    assert torch.all(lbuf[:G] == 7.0) and torch.all(lbuf[G + n_l:] == 7.0)
+    o, l = to_np(out, lse, inp)
+    check(inp, o, l)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_deterministic(cfg):
+    inp = inputs.draw_config(cfg)
+    o1, l1 = gpu_run(inp)
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2 = gpu_run(inp)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def test_side_stream():
+    inp = inputs.draw(1, 2, 260, 128, "fp16", False, seed=28)
+    s = torch.cuda.Stream()
+    q, k, v, _ = binding.to_device(inp)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        announce("side stream " + inp.describe())
+        o, l = binding.fwd(q, k, v, causal=False, scale=inp.scale)
+    s.synchronize()
+    on, ln = to_np(o, l, inp)
+    check(inp, on, ln)
+
+
+def test_binding_rejects_bad_tensors():
+    x = torch.zeros((1, 1, 8, 96), dtype=torch.float16, device="cuda")
+    with pytest.raises(binding.FAError):
+        binding.fwd(x, x, x)  # d = 96 refused by the library
+    y = torch.zeros((1, 1, 8, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        binding.fwd(y, y, y)
