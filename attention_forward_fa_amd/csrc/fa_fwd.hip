@@ -12,8 +12,11 @@
 // counterpart here and is not imitated):
 //   * workgroup = 4 waves of 64 lanes; each wave owns 32 query rows, so a
 //     workgroup covers BR = 128 rows of one (b, h) head;
-//   * K/V blocks of BC = 64 keys are staged global -> VGPR -> LDS; the global
-//     loads for block j+1 are in flight while block j is computed;
+//   * K/V blocks of BC = 64 keys go global -> VGPR -> LDS through buffer
+//     loads (a per-head buffer resource returns zeros past row N, so ragged
+//     tails need no bounds branches); LDS is double-buffered, one barrier per
+//     block, and the global loads of block j+2 are in flight while block j is
+//     computed;
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{f16,bf16} (or the fp8 v_mfma_scale_f32_32x32x64
 //     with unit block scales).  In the 32x32 accumulator layout a lane owns
@@ -23,9 +26,13 @@
 //   * the same accumulator registers, rounded to fp16, are already the B
 //     operand of O^T += V^T P^T: the key order inside one MFMA's contraction
 //     is free, so P never moves between lanes or through LDS;
-//   * V is transposed (and converted to fp16) while it is staged, so the A
-//     operand of the PV product is two 8-byte LDS reads per lane;
-//   * LDS rows are padded so the operand reads are free of bank conflicts.
+//   * V stays row-major in LDS (converted to fp16 for bf16 / fp8 inputs on
+//     the way in); ds_read_b64_tr_b16 delivers the transposed V^T operand;
+//   * LDS rows carry an XOR swizzle of their 16-byte chunks so the operand
+//     reads are free of bank conflicts without padding;
+//   * the reference max of a row only moves when a block max exceeds it by
+//     more than 2^8, so the O rescale is skipped for almost every block
+//     (probabilities then stay <= 2^8 and O, l remain consistent).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -41,8 +48,10 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kQW = 32;            // query rows per wave
 constexpr int kBR = kQW * kWaves;  // query rows per workgroup
 constexpr int kBC = 64;            // keys per K/V block
-constexpr int kKPad = 16;          // bytes of padding per K row in LDS
-constexpr int kVPad = 4;           // halfs of padding per V^T row in LDS
+// The reference max of a row moves only when a block max passes it by more
+// than this many powers of two, bounding every probability by 2^8 (fine for
+// fp16 P) while skipping nearly all accumulator rescales.
+constexpr float kRescaleLog2 = 8.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -53,6 +62,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
 // Input element type: 0 fp16, 1 bf16, 2 fp8 e4m3.
 template <int DT>
@@ -98,12 +108,14 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Lanes l and l^32 hold the same query.  v_permlane32_swap with both operands
 // equal to x leaves each lane holding {x[l], x[l^32]} across its two results,
 // so a symmetric combination of the pair reduces over the two lanes.
 __device__ __forceinline__ float max_pair32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float sum_pair32(float x) {
@@ -143,37 +155,60 @@ struct Params {
   const float* descale_v;
   _Float16* o;
   float* lse;
-  int H;
   int N;
   int n_qtiles;
   int bh;  // B*H
   float scale;
 };
 
+// Buffer resource over one head's [N, row_bytes] slice: loads past the end
+// return zeros, which is how ragged tails are read without bounds branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, nbytes,
+                                           0x00020000);
+}
+
+// LDS rows are stored with their 16-byte chunks permuted by an XOR swizzle,
+// chunk' = chunk ^ f(row), f(row) = 5 * (row / P) mod CPR, where CPR is the
+// number of chunks in a row and P = 256 / row_bytes rows share one pass over
+// the 64 banks.  f has period 16 in row.  It makes the MFMA operand reads
+// conflict-free: 16 consecutive rows read at one logical chunk hit 16
+// distinct bank groups, and the 8 rows x 64 bytes of a transposed V read
+// spread evenly over the banks.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+  constexpr int CPR = ROWB / 16;
+  constexpr int P = ROWB >= 256 ? 1 : 256 / ROWB;
+  return (5 * (row / P)) & (CPR - 1);
+}
+
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int ES = E::bytes;
-  constexpr int KROW = D * ES + kKPad;          // bytes per K row in LDS
-  constexpr int VROW = kBC + kVPad;             // halfs per V^T row in LDS
-  constexpr int NKS = D / E::kstep;             // QK^T MFMAs per 32x32 tile
-  constexpr int NDT = D / 32;                   // 32-wide d tiles of O^T
-  constexpr int K_CHUNKS = kBC * D * ES / 16;   // 16-byte chunks in a K block
-  constexpr int K_PER_T = K_CHUNKS / kThreads;  // per thread
-  constexpr int K_CHUNKS_ROW = D * ES / 16;
-  constexpr int VD = D / 16;                    // d values per thread in V staging
-  constexpr int VBYTES = VD * ES;               // bytes per key row per thread
-  constexpr int VWORDS = (VBYTES + 3) / 4;
-  static_assert(K_CHUNKS % kThreads == 0, "K staging must tile the workgroup");
+  constexpr int KROWB = D * ES;           // bytes per K row, global and LDS
+  constexpr int VROWB = D * 2;            // bytes per V row in LDS (fp16)
+  constexpr int KCPR = KROWB / 16;        // 16-byte chunks per K row
+  constexpr int VCPR = VROWB / 16;        // fp16 chunks (8 values) per V row
+  constexpr int KBUF = kBC * KROWB;       // bytes of one K stage
+  constexpr int VBUF = kBC * VROWB;       // bytes of one V stage
+  constexpr int NKS = D / E::kstep;       // QK^T MFMAs per 32x32 score tile
+  constexpr int NDT = D / 32;             // 32-row d tiles of O^T
+  constexpr int K_PER_T = kBC * KCPR / kThreads;
+  constexpr int V_PER_T = kBC * VCPR / kThreads;
+  constexpr int VIN = 8 * ES;             // input bytes behind one fp16 V chunk
+  static_assert(K_PER_T >= 1 && kBC * KCPR % kThreads == 0, "K staging must tile the block");
+  static_assert(V_PER_T >= 1 && kBC * VCPR % kThreads == 0, "V staging must tile the block");
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBC * KROW];
-  __shared__ __attribute__((aligned(16))) _Float16 vt_lds[D * VROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * KBUF + 2 * VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lr = lane & 31;   // row/column index inside a 32x32 MFMA tile
-  const int hh = lane >> 5;   // which half of the wave
+  const int lr = lane & 31;   // row/column inside a 32x32 MFMA tile
+  const int hh = lane >> 5;   // half of the wave
 
   // ---- work decomposition: one workgroup per (b*H + h, query tile) ----------
   const int wg = blockIdx.x;
@@ -189,15 +224,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   }
   const int N = p.N;
   const int64_t head_off = (int64_t)bh * N * D;
-  const uint8_t* qg = p.q + head_off * ES;
-  const uint8_t* kg = p.k + head_off * ES;
-  const uint8_t* vg = p.v + head_off * ES;
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + head_off * ES, N * KROWB);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + head_off * ES, N * KROWB);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v + head_off * ES, N * KROWB);
 
-  const int q0 = qt * kBR;                 // first query row of the workgroup
-  const int qw0 = q0 + wave * kQW;         // first query row of this wave
-  const int my_q = qw0 + lr;               // the query this lane's column holds
+  const int q0 = qt * kBR;              // first query row of the workgroup
+  const int qw0 = q0 + wave * kQW;      // first query row of this wave
+  const int my_q = qw0 + lr;            // the query held by this lane's column
 
-  float c = p.scale * kLog2e;  // exp(x) = exp2(x * log2 e)
+  float c = p.scale * kLog2e;           // exp(x) = exp2(x log2 e)
   float v_scale = 1.0f;
   if constexpr (DT == FA_DTYPE_FP8_E4M3) {
     if (p.descale_q) {
@@ -206,208 +241,242 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     }
   }
 
-  // ---- Q tile -> registers, laid out as the B operand of S^T = K Q^T ---------
+  // ---- Q tile -> registers, the B operand of S^T = K Q^T (rows >= N read 0) --
   QKOperand<DT> qreg[NKS];
-  {
-    const bool ok = my_q < N;
-    const uint8_t* src = qg + (int64_t)(ok ? my_q : 0) * D * ES;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int byte = (ks * E::kstep + hh * (E::kstep / 2)) * ES;
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int byte = (ks * E::kstep + hh * (E::kstep / 2)) * ES;
 #pragma unroll
-      for (int w = 0; w < E::opnd_dwords; w += 4) {
-        u32x4 x = ok ? *reinterpret_cast<const u32x4*>(src + byte + 4 * w) : u32x4{0, 0, 0, 0};
-        qreg[ks].w[w + 0] = x[0];
-        qreg[ks].w[w + 1] = x[1];
-        qreg[ks].w[w + 2] = x[2];
-        qreg[ks].w[w + 3] = x[3];
-      }
+    for (int w = 0; w < E::opnd_dwords; w += 4) {
+      u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, my_q * KROWB + byte + 4 * w, 0, 0);
+      qreg[ks].w[w + 0] = x[0];
+      qreg[ks].w[w + 1] = x[1];
+      qreg[ks].w[w + 2] = x[2];
+      qreg[ks].w[w + 3] = x[3];
     }
   }
 
-  // ---- number of K/V blocks this workgroup visits -----------------------------
+  // ---- K/V blocks this workgroup visits --------------------------------------
   int kv_end = N;
   if constexpr (CAUSAL) kv_end = min(N, q0 + kBR);
   const int nblk = (kv_end + kBC - 1) / kBC;
 
-  // ---- staging registers ----------------------------------------------------
+  // ---- staging: per-thread global offsets and swizzled LDS offsets ------------
+  int k_goff[K_PER_T], k_loff[K_PER_T];
+#pragma unroll
+  for (int i = 0; i < K_PER_T; ++i) {
+    const int ch = tid + i * kThreads;
+    const int row = ch / KCPR, lc = ch % KCPR;
+    k_goff[i] = row * KROWB + lc * 16;
+    k_loff[i] = row * KROWB + ((lc ^ swz<KROWB>(row)) * 16);
+  }
+  int v_goff[V_PER_T], v_loff[V_PER_T];
+#pragma unroll
+  for (int i = 0; i < V_PER_T; ++i) {
+    const int ch = tid + i * kThreads;
+    const int row = ch / VCPR, lc = ch % VCPR;
+    v_goff[i] = row * KROWB + lc * VIN;
+    v_loff[i] = 2 * KBUF + row * VROWB + ((lc ^ swz<VROWB>(row)) * 16);
+  }
   u32x4 kst[K_PER_T];
-  uint32_t vst[4][VWORDS];
-  const int va = tid / 16;  // keys 4*va .. 4*va+3 of the block
-  const int vc = tid % 16;  // d values vc*VD .. vc*VD+VD-1
+  u32x4 vst[V_PER_T];  // fp16 after conversion (fp8 uses the low half on load)
 
   auto load_block = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / K_CHUNKS_ROW;
-      const int col = ch % K_CHUNKS_ROW;
-      const int key = kb + row;
-      kst[i] = key < N ? *reinterpret_cast<const u32x4*>(kg + ((int64_t)key * D * ES) + col * 16)
-                       : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < K_PER_T; ++i)
+      kst[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_goff[i], kb * KROWB, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kb + 4 * va + r;
-      const uint8_t* src = vg + (int64_t)key * D * ES + vc * VBYTES;
-      if constexpr (VBYTES == 16) {
-        u32x4 x = key < N ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
-        vst[r][0] = x[0]; vst[r][1] = x[1]; vst[r][2] = x[2]; vst[r][3] = x[3];
-      } else if constexpr (VBYTES == 8) {
-        u32x2 x = key < N ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
-        vst[r][0] = x[0]; vst[r][1] = x[1];
+    for (int i = 0; i < V_PER_T; ++i) {
+      if constexpr (VIN == 16) {
+        vst[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_goff[i], kb * KROWB, 0);
       } else {
-        vst[r][0] = key < N ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+        u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(vrs, v_goff[i], kb * KROWB, 0);
+        vst[i] = u32x4{x[0], x[1], 0u, 0u};
       }
     }
   };
 
-  auto store_block = [&]() {
+  auto store_block = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int ch = tid + i * kThreads;
-      const int row = ch / K_CHUNKS_ROW;
-      const int col = ch % K_CHUNKS_ROW;
-      *reinterpret_cast<u32x4*>(k_lds + row * KROW + col * 16) = kst[i];
-    }
-    // V: 4 keys x VD d values -> VD rows of V^T, 4 consecutive keys each.
-    uint32_t f16w[4][VD / 2];  // fp16 pairs along d, per key
+    for (int i = 0; i < K_PER_T; ++i)
+      *reinterpret_cast<u32x4*>(lds + buf * KBUF + k_loff[i]) = kst[i];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int i = 0; i < V_PER_T; ++i) {
+      u32x4 h;
+      if constexpr (DT == FA_DTYPE_FP16) {
+        h = vst[i];
+      } else if constexpr (DT == FA_DTYPE_BF16) {
 #pragma unroll
-      for (int w = 0; w < VD / 2; ++w) {
-        if constexpr (ES == 2) {
-          f16w[r][w] = v_pair_to_f16<DT, false>(vst[r][w]);
-        } else if (w & 1) {
-          f16w[r][w] = v_pair_to_f16<DT, true>(vst[r][w / 2]);
-        } else {
-          f16w[r][w] = v_pair_to_f16<DT, false>(vst[r][w / 2]);
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < VD; ++e) {
-      const int w = e / 2;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (f16w[0][w] >> 16) | (f16w[1][w] & 0xffff0000u);
-        hi = (f16w[2][w] >> 16) | (f16w[3][w] & 0xffff0000u);
+        for (int w = 0; w < 4; ++w) h[w] = v_pair_to_f16<DT, false>(vst[i][w]);
       } else {
-        lo = (f16w[0][w] & 0xffffu) | (f16w[1][w] << 16);
-        hi = (f16w[2][w] & 0xffffu) | (f16w[3][w] << 16);
+        h[0] = v_pair_to_f16<DT, false>(vst[i][0]);
+        h[1] = v_pair_to_f16<DT, true>(vst[i][0]);
+        h[2] = v_pair_to_f16<DT, false>(vst[i][1]);
+        h[3] = v_pair_to_f16<DT, true>(vst[i][1]);
       }
-      *reinterpret_cast<u32x2*>(vt_lds + (vc * VD + e) * VROW + 4 * va) = u32x2{lo, hi};
+      *reinterpret_cast<u32x4*>(lds + buf * VBUF + v_loff[i]) = h;
     }
   };
+
+  // ---- per-lane LDS operand addresses (block-independent parts) -------------
+  // K (A operand of S^T): row kt*32 + lr, logical chunk(s) of k-step ks.
+  constexpr int KCH = E::opnd_dwords / 4;  // 16-byte chunks per operand
+  int k_raddr[NKS][KCH];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int lc = (ks * E::kstep + hh * (E::kstep / 2)) * ES / 16 + u;
+      k_raddr[ks][u] = lr * KROWB + ((lc ^ swz<KROWB>(lr)) * 16);
+    }
+  // V (A operand of O^T = V^T P^T) via ds_read_b64_tr_b16.  In each group of
+  // 16 lanes, lane 4e + r reads 4 d-values (4r..4r+3 of the group's 16) of
+  // key K0 + e; the transposed read hands lane i the 4 keys K0..K0+3 at d-value
+  // i.  Group g covers d-values 16*(g%2) .. +15 of a 32-row d tile and keys
+  // 4*(g/2) .. +3 of each 8-key half.
+  int v_raddr[NDT][2];
+  {
+    const int grp = lane >> 4, li = lane & 15;
+    const int e = li >> 2, r = li & 3;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key = 8 * half + 4 * (grp >> 1) + e;
+        const int d = t * 32 + 16 * (grp & 1) + 4 * r;
+        const int lc = d / 8;
+        v_raddr[t][half] = 2 * KBUF + key * VROWB + ((lc ^ swz<VROWB>(key)) * 16) + (d % 8) * 2;
+      }
+  }
 
   // ---- running softmax state and the O^T accumulator --------------------------
   f32x16 acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
-  float m_run = -INFINITY;  // running max of the raw scores q.k of this query
-  float l_run = 0.0f;       // this lane's share of the running row sum
+  // m_run: the reference max of this query's raw scores q.k that probabilities
+  // are taken against.  It only moves when the block max exceeds it by more
+  // than kRescaleLog2 in log2 units: until then p = exp2(c s - c m_run) stays
+  // <= 2^kRescaleLog2 and O, l are consistent without a rescale.
+  float m_run = -INFINITY;
+  float l_run = 0.0f;  // this lane's share of the row sum, relative to m_run
 
   load_block(0);
+  store_block(0);
+  if (nblk > 1) load_block(kBC);
+  __syncthreads();
+
   for (int j = 0; j < nblk; ++j) {
     const int kb = j * kBC;
-    __syncthreads();  // every wave is done reading the previous block
-    store_block();
+    const int buf = j & 1;
+    const uint8_t* kbuf = lds + buf * KBUF;
+    const uint8_t* vbuf = lds + buf * VBUF;
+
+    // A wave whose rows all precede this block has nothing to compute in it.
+    if (!(CAUSAL && kb > qw0 + kQW - 1)) {
+      // S^T = K_j Q^T: two 32-key tiles of this wave's 32 queries.
+      f32x16 st[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        st[kt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          QKOperand<DT> a;
+#pragma unroll
+          for (int u = 0; u < KCH; ++u) {
+            u32x4 x = *reinterpret_cast<const u32x4*>(kbuf + kt * 32 * KROWB + k_raddr[ks][u]);
+            a.w[4 * u + 0] = x[0]; a.w[4 * u + 1] = x[1];
+            a.w[4 * u + 2] = x[2]; a.w[4 * u + 3] = x[3];
+          }
+          st[kt] = mfma_qk<DT>(a, qreg[ks], st[kt]);
+        }
+      }
+
+      // Keys past N, and (causal) keys after the query, are masked out.
+      const bool need_mask = (kb + kBC > N) || (CAUSAL && kb + kBC - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb + kt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+            bool keep = key < N;
+            if constexpr (CAUSAL) keep = keep && key <= my_q;
+            st[kt][i] = keep ? st[kt][i] : -INFINITY;
+          }
+      }
+
+      // Block row max (in-lane over 32 keys, then across the lane pair).  The
+      // IEEE maximum builtin lowers to one v_maximum3_f32 per two scores.
+      float mx = st[0][0];
+#pragma unroll
+      for (int i = 1; i < 15; i += 2) mx = vmax(vmax(mx, st[0][i]), st[0][i + 1]);
+      mx = vmax(mx, st[0][15]);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = vmax(vmax(mx, st[1][i]), st[1][i + 1]);
+      mx = max_pair32(mx);
+
+      // Move the reference max only when some row's block max passed it by
+      // more than the margin (wave-uniform branch).
+      const bool grow = (mx - m_run) * c > kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
+      }
+      const float mc = m_run * c;
+
+      float rs = 0.0f;
+      uint32_t pw[2][2][4];  // [kt][k-step][dword] fp16 pairs: B operand of O^T += V^T P^T
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][i], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][i + 1], c, -mc));
+          rs += p0 + p1;
+          pw[kt][i / 8][(i % 8) / 2] = pack_f16x2(p0, p1);
+        }
+      l_run += rs;
+
+      // O^T += V^T P^T.  Slot j of lane half hh in k-step s of key tile kt is
+      // key kt*32 + 16*s + 8*(j/4) + 4*hh + (j%4), the order the S^T
+      // accumulator already holds; the transposed V reads follow it.
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int krow = (kt * 32 + 16 * s) * VROWB;
+            short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4_t*)(vbuf + krow + v_raddr[t][0]));
+            short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4_t*)(vbuf + krow + v_raddr[t][1]));
+            u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+            u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+            u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+            u32x4 b = {pw[kt][s][0], pw[kt][s][1], pw[kt][s][2], pw[kt][s][3]};
+            acc[t] = mfma_pv(a, b, acc[t]);
+          }
+    }
+
+    // Stage block j+1 into the other buffer (its readers all passed the last
+    // barrier), then start the global loads of block j+2.
+    if (j + 1 < nblk) store_block(buf ^ 1);
+    if (j + 2 < nblk) load_block(kb + 2 * kBC);
     __syncthreads();
-    if (j + 1 < nblk) load_block(kb + kBC);
-
-    // A wave whose rows all precede this block has nothing to do in it.
-    if (CAUSAL && kb > qw0 + kQW - 1) continue;
-
-    // S^T = K_j Q^T: two 32-key tiles of this wave's 32 queries.
-    f32x16 st[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      st[kt] = f32x16{};
-      const uint8_t* krow = k_lds + (kt * 32 + lr) * KROW;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        QKOperand<DT> a;
-        const int byte = (ks * E::kstep + hh * (E::kstep / 2)) * ES;
-#pragma unroll
-        for (int w = 0; w < E::opnd_dwords; w += 4) {
-          u32x4 x = *reinterpret_cast<const u32x4*>(krow + byte + 4 * w);
-          a.w[w + 0] = x[0]; a.w[w + 1] = x[1]; a.w[w + 2] = x[2]; a.w[w + 3] = x[3];
-        }
-        st[kt] = mfma_qk<DT>(a, qreg[ks], st[kt]);
-      }
-    }
-
-    // Mask keys past N, and (causal) keys after the query.
-    const bool need_mask = (kb + kBC > N) || (CAUSAL && kb + kBC - 1 > qw0);
-    if (need_mask) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + kt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-          bool keep = key < N;
-          if constexpr (CAUSAL) keep = keep && key <= my_q;
-          st[kt][i] = keep ? st[kt][i] : -INFINITY;
-        }
-      }
-    }
-
-    // Online softmax: new running max, rescale factor, probabilities.
-    float mx = st[0][0];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int i = (kt == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
-    }
-    mx = max_pair32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    const float mc = m_new * c;
-    m_run = m_new;
-
-    float rs = 0.0f;
-    uint32_t pw[2][2][4];  // [kt][k-step][dword] fp16 pairs: B operand of O^T += V^T P^T
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][i], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][i + 1], c, -mc));
-        rs += p0 + p1;
-        pw[kt][i / 8][(i % 8) / 2] = pack_f16x2(p0, p1);
-      }
-    }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
-
-    // O^T += V^T P^T.  Slot j of lane half hh in k-step s of key tile kt holds
-    // key kt*32 + 16*s + 8*(j/4) + 4*hh + (j%4), matching the S^T layout.
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-      const _Float16* vrow = vt_lds + (t * 32 + lr) * VROW;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int key0 = kt * 32 + 16 * s + 4 * hh;
-          u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + key0);
-          u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + key0 + 8);
-          u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          u32x4 b = {pw[kt][s][0], pw[kt][s][1], pw[kt][s][2], pw[kt][s][3]};
-          acc[t] = mfma_pv(a, b, acc[t]);
-        }
-      }
-    }
   }
 
-  // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m*c + log2 l) ---------------
+  // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
   if (my_q < N) {
     const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;
     _Float16* orow = p.o + head_off + (int64_t)my_q * D;
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) {
+    for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = t * 32 + 8 * g + 4 * hh;
@@ -415,10 +484,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
                    pack_f16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
-    }
-    if (hh == 0) {
-      p.lse[(int64_t)bh * N + my_q] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
-    }
+    if (hh == 0) p.lse[(int64_t)bh * N + my_q] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
   }
 }
 
@@ -444,7 +510,8 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   }
   // Index arithmetic: rows of one tensor fit in int32, elements in int64;
   // the grid (B*H query-tile rows) fits in int32.
-  if (N > (int64_t)1 << 24 || B * H > (int64_t)1 << 24) return FA_ERR_SHAPE;
+  // One head's rows must stay addressable by 32-bit buffer offsets.
+  if (N > (int64_t)1 << 22 || B * H > (int64_t)1 << 24) return FA_ERR_SHAPE;
   const int64_t tiles = (N + kBR - 1) / kBR;
   if (B * H * tiles > INT32_MAX) return FA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
@@ -481,7 +548,6 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   prm.descale_v = dv;
   prm.o = static_cast<_Float16*>(o);
   prm.lse = lse;
-  prm.H = (int)H;
   prm.N = (int)N;
   prm.n_qtiles = (int)((N + kBR - 1) / kBR);
   prm.bh = (int)(B * H);

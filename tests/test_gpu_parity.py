@@ -4,6 +4,8 @@ Bars (absolute, element-wise, O upcast to float64 against the oracle's exact O):
   fp16 / bf16:  max|dO| <= 4e-3, mean|dO| <= 5e-4, max|dLSE| <= 1e-3
   fp8 (e4m3):   max|dO| <= 3e-2, mean|dO| <= 3.75e-3, max|dLSE| <= 1e-3
 """
+import json
+import os
 import sys
 
 import numpy as np
@@ -56,6 +58,12 @@ def check(inp, o, l, heads=None, rows=None, tol=None):
     msg = (f"{inp.describe()}: max|dO|={d_o.max():.3e} mean|dO|={d_o.mean():.3e} "
            f"max|dLSE|={d_l.max():.3e}")
     announce(msg)
+    log = os.environ.get("FA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": inp.describe(), "max_dO": float(d_o.max()),
+                                "mean_dO": float(d_o.mean()), "max_dLSE": float(d_l.max()),
+                                "rows": int(len(rsel)), "heads": int(len(hsel))}) + "\n")
     assert d_o.max() <= mx_o, msg
     assert d_o.mean() <= mean_o, msg
     assert d_l.max() <= mx_l, msg
@@ -147,10 +155,13 @@ def test_causal_row0_is_v0_exactly(dtype, d):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
 def test_large_scores(dtype):
-    # Scores of several hundred: the running max must be subtracted before exp.
+    # Scores of order 100 (beyond fp32 exp overflow at ~88): the running max
+    # must be subtracted before exp.  Scores are float32 dot products, so the
+    # LSE bar here is relative to |LSE|: 1e-3 + 1e-4 |LSE|.
     inp = inputs.draw(1, 2, 130, 64, dtype, False, seed=24, scale=4.0)
     o, l = to_np(*gpu_run(inp), inp)
-    tol = (TOL[dtype][0], TOL[dtype][1], 1e-3 * max(1.0, float(np.abs(l).max()) / 100))
+    assert float(np.abs(l).max()) > 88.0
+    tol = (TOL[dtype][0], TOL[dtype][1], 1e-3 + 1e-4 * float(np.abs(l).max()))
     check(inp, o, l, tol=tol)
 
 
