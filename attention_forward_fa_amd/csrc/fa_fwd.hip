@@ -184,6 +184,35 @@ __device__ __forceinline__ int swz(int row) {
 
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
+// Workgroup -> (head, query tile).  Workgroups are dispatched round-robin over
+// the 8 XCDs (workgroup w runs on XCD w % 8), and each XCD has its own L2.  When
+// the head count is a multiple of 8, XCD x gets heads x, x+8, x+16, ... so all
+// query tiles of a head, which re-read the same K and V, share one L2.  Within
+// an XCD, causal work goes longest tiles first (the last query tile of each of
+// its heads, then the one before, ...); non-causal work goes head by head.
+__device__ __forceinline__ void tile_of(int w, int n_heads, int n_tiles, bool causal, int& bh,
+                                        int& qt) {
+  constexpr int kXcd = 8;
+  int head_slot, rank, heads_here, xcd = 0, stride = 1;
+  if (n_heads % kXcd == 0) {
+    xcd = w % kXcd;
+    w /= kXcd;
+    heads_here = n_heads / kXcd;
+    stride = kXcd;
+  } else {
+    heads_here = n_heads;
+  }
+  if (causal) {
+    head_slot = w % heads_here;
+    rank = w / heads_here;
+    qt = n_tiles - 1 - rank;
+  } else {
+    head_slot = w / n_tiles;
+    qt = w % n_tiles;
+  }
+  bh = head_slot * stride + xcd;
+}
+
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   using E = Elem<DT>;
@@ -211,17 +240,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   const int hh = lane >> 5;   // half of the wave
 
   // ---- work decomposition: one workgroup per (b*H + h, query tile) ----------
-  const int wg = blockIdx.x;
   int bh, qt;
-  if constexpr (CAUSAL) {
-    // Longest tiles first: the last query tile of every head, then the one
-    // before it, and so on.
-    bh = wg % p.bh;
-    qt = p.n_qtiles - 1 - wg / p.bh;
-  } else {
-    bh = wg / p.n_qtiles;
-    qt = wg % p.n_qtiles;
-  }
+  tile_of(blockIdx.x, p.bh, p.n_qtiles, CAUSAL, bh, qt);
   const int N = p.N;
   const int64_t head_off = (int64_t)bh * N * D;
   const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + head_off * ES, N * KROWB);

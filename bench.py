@@ -39,7 +39,25 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every workload and print one line each to stderr")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run plain device copies of MIB MiB (the "
+                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args(argv)
+
+
+def copy_calibration(mib, steps):
+    """Plain device-to-device copies of a known size: MIB MiB read + MIB MiB written."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "launches": steps,
+                      "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4}))
+    return 0
 
 
 def time_gpu(inp, steps, warmup):
@@ -97,6 +115,30 @@ def cpu_baseline(inp, budget_s):
                       f"fp64 numpy/BLAS, {dt:.1f} s"}
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_fwd_fp16_d128_n4096_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "attention_forward_fa_amd", "csrc", "fa_fwd.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE profile, or None
+    when that profile is for another workload or an older kernel source."""
+    import hashlib
+    if workload != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    vals, sha = {}, None
+    for line in open(TRAFFIC_PROFILE, encoding="utf-8"):
+        if "source_sha256_16:" in line:
+            sha = line.split("source_sha256_16:")[1].split()[0]
+        elif line.strip() and not line.startswith("#"):
+            k, v = line.split()[:2]
+            vals[k] = float(v)
+    cur = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    if sha != cur:
+        return None
+    return int(vals["fetch_kib_per_dispatch"] * 1024 * vals["fetch_scale"]
+               + vals["write_kib_per_dispatch"] * 1024 * vals["write_scale"])
+
+
 def describe(inp, sec):
     from attention_forward_fa_amd import accounting as acc
 
@@ -121,6 +163,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, args.steps)
     name, B, H, N, d, dtype, causal, seed = inputs.config(args.workload)
     inp = inputs.draw(B, H, N, d, dtype, causal, seed)
     sec = time_gpu(inp, args.steps, args.warmup)
@@ -150,7 +194,8 @@ def main(argv=None):
                    "input_dtype": dtype, "causal": bool(causal), "seed": seed,
                    "outputs": "O fp16 + LSE fp32", "accumulate": "fp32"},
         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                     "traffic": measured_traffic(name)},
         "frac_of_peak": round(tf / peak, 4),
         "algorithmic_bytes": acc.algorithmic_bytes(B, H, N, d, dtype),
     }
