@@ -53,7 +53,8 @@ def load_library(path: Optional[str] = None):
     with _lock:
         if _lib is not None and path is None:
             return _lib
-        p = path or LIB_PATH
+        # FA_MI355X_LIBRARY names an alternative build of the same library.
+        p = path or os.environ.get("FA_MI355X_LIBRARY") or LIB_PATH
         if not os.path.exists(p):
             raise FileNotFoundError(
                 f"{p} is missing: build it first (python -m attention_forward_fa_amd.build)")

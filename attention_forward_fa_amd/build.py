@@ -1,6 +1,7 @@
 """Build of the HIP library libfa_mi355x.so for gfx950 (runs on any host with hipcc)."""
 from __future__ import annotations
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -42,6 +43,9 @@ def build(verbose: bool = False, extra=()) -> str:
             print(res.stdout[-20000:], res.stderr[-20000:])
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed with status {res.returncode}")
+        # Bind every symbol now: a kernel whose host stub is missing shows up
+        # here as an undefined symbol instead of at the first call.
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
         os.replace(tmp, LIB_PATH)
     finally:
         if os.path.exists(tmp):

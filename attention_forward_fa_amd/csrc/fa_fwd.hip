@@ -43,7 +43,8 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;          // two waves per SIMD, in two groups of four
+constexpr int kGroupWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kQW = 32;            // query rows per wave
 constexpr int kBR = kQW * kWaves;  // query rows per workgroup
@@ -109,6 +110,22 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Scheduling shape for a run of NM MFMAs fed by RPM LDS reads each: the reads
+// of the first LA MFMAs go first, then every MFMA is followed by the reads of
+// the MFMA LA places later.  Without it the compiler issues each read right
+// before its MFMA and every MFMA waits out the full LDS latency.
+template <int NM, int RPM, int LA>
+__device__ __forceinline__ void mfma_read_pipeline() {
+  static_assert(LA <= NM, "look-ahead longer than the run");
+  __builtin_amdgcn_sched_group_barrier(0x100, RPM * LA, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < NM - LA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
 
 // Lanes l and l^32 hold the same query.  v_permlane32_swap with both operands
 // equal to x leaves each lane holding {x[l], x[l^32]} across its two results,
@@ -183,6 +200,14 @@ __device__ __forceinline__ int swz(int row) {
 }
 
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from a buffer straight into LDS: lane t writes
+// lds_dst + 16 t (lds_dst must be wave-uniform); past-the-end lanes write 0.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds_dst,
+                                                int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_dst, 16, voffset, soffset, 0, 0);
+}
 
 // Workgroup -> (head, query tile).  Workgroups are dispatched round-robin over
 // the 8 XCDs (workgroup w runs on XCD w % 8), and each XCD has its own L2.  When
@@ -218,24 +243,28 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int ES = E::bytes;
   constexpr int KROWB = D * ES;           // bytes per K row, global and LDS
-  constexpr int VROWB = D * 2;            // bytes per V row in LDS (fp16)
   constexpr int KCPR = KROWB / 16;        // 16-byte chunks per K row
-  constexpr int VCPR = VROWB / 16;        // fp16 chunks (8 values) per V row
   constexpr int KBUF = kBC * KROWB;       // bytes of one K stage
-  constexpr int VBUF = kBC * VROWB;       // bytes of one V stage
+  // V is stored transposed, V^T[d][key] in fp16, one row of kBC keys per d
+  // value, padded by 16 bytes so that 16 consecutive rows read at one column
+  // hit distinct banks.  Inside every group of 16 keys the two middle quads
+  // are swapped (keys 0-3, 8-11, 4-7, 12-15), so the 8 keys one lane feeds to
+  // a P V MFMA are contiguous.
+  constexpr int VTROW = kBC * 2 + 16;     // bytes per V^T row
+  constexpr int VBUF = D * VTROW;         // bytes of one V stage
   constexpr int NKS = D / E::kstep;       // QK^T MFMAs per 32x32 score tile
   constexpr int NDT = D / 32;             // 32-row d tiles of O^T
-  constexpr int K_PER_T = kBC * KCPR / kThreads;
-  constexpr int V_PER_T = kBC * VCPR / kThreads;
-  constexpr int VIN = 8 * ES;             // input bytes behind one fp16 V chunk
-  static_assert(K_PER_T >= 1 && kBC * KCPR % kThreads == 0, "K staging must tile the block");
-  static_assert(V_PER_T >= 1 && kBC * VCPR % kThreads == 0, "V staging must tile the block");
+  constexpr int K_INSTR = kBC * KCPR / kWave;  // 64-lane LDS-load instructions per K stage
+  constexpr int VD = D / 16;              // d values per staging thread (4 keys each)
+  constexpr int VIN = VD * ES;            // input bytes per key row per staging thread
+  static_assert(kBC * D == 4 * VD * kGroupWaves * kWave, "V staging must tile the staging waves");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * KBUF + 2 * VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int group = wave / kGroupWaves;  // 0 runs one phase ahead of 1
   const int lr = lane & 31;   // row/column inside a 32x32 MFMA tile
   const int hh = lane >> 5;   // half of the wave
 
@@ -281,62 +310,90 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   if constexpr (CAUSAL) kv_end = min(N, q0 + kBR);
   const int nblk = (kv_end + kBC - 1) / kBC;
 
-  // ---- staging: per-thread global offsets and swizzled LDS offsets ------------
-  int k_goff[K_PER_T], k_loff[K_PER_T];
+  // ---- staging -----------------------------------------------------------------
+  // The four waves of group 0 stage every block.  K goes global -> LDS directly
+  // (buffer_load ... lds): one instruction fills 64 consecutive 16-byte LDS
+  // slots, lane t slot t; slot s of a stage holds row s / KCPR, physical
+  // chunk s % KCPR, so each lane fetches the logical chunk the swizzle puts
+  // there.  V goes through registers: staging thread (quad, dgrp) loads keys
+  // 4*quad .. +3 at d values dgrp*VD .. +VD-1, converts them to fp16 and
+  // writes VD rows of V^T, 4 keys (8 bytes) each.
+  constexpr int kStagers = kGroupWaves;
+  constexpr int K_PER_W = (K_INSTR + kStagers - 1) / kStagers;
+  const int stid = (wave % kStagers) * kWave + lane;  // staging thread id, 0..255
+  int k_goff[K_PER_W];
 #pragma unroll
-  for (int i = 0; i < K_PER_T; ++i) {
-    const int ch = tid + i * kThreads;
-    const int row = ch / KCPR, lc = ch % KCPR;
-    k_goff[i] = row * KROWB + lc * 16;
-    k_loff[i] = row * KROWB + ((lc ^ swz<KROWB>(row)) * 16);
+  for (int u = 0; u < K_PER_W; ++u) {
+    const int slot = (u * kStagers + wave % kStagers) * kWave + lane;
+    const int row = slot / KCPR, phys = slot % KCPR;
+    k_goff[u] = row * KROWB + ((phys ^ swz<KROWB>(row)) * 16);
   }
-  int v_goff[V_PER_T], v_loff[V_PER_T];
-#pragma unroll
-  for (int i = 0; i < V_PER_T; ++i) {
-    const int ch = tid + i * kThreads;
-    const int row = ch / VCPR, lc = ch % VCPR;
-    v_goff[i] = row * KROWB + lc * VIN;
-    v_loff[i] = 2 * KBUF + row * VROWB + ((lc ^ swz<VROWB>(row)) * 16);
+  const int vquad = stid % 16, vdgrp = stid / 16;
+  const int v_goff = 4 * vquad * KROWB + vdgrp * VIN;
+  int v_loff;
+  {
+    const int qq = vquad % 4;  // quad inside its 16-key group -> position quad
+    const int keypos = 16 * (vquad / 4) + 4 * ((qq >> 1) + 2 * (qq & 1));
+    v_loff = 2 * KBUF + vdgrp * VD * VTROW + keypos * 2;
   }
-  u32x4 kst[K_PER_T];
-  u32x4 vst[V_PER_T];  // fp16 after conversion (fp8 uses the low half on load)
+  constexpr int VW = (VIN + 3) / 4;  // dwords of one key row of a staging thread
+  uint32_t vst[4][VW];
 
-  auto load_block = [&](int kb) {
+  auto load_k = [&](int kb, int buf) {
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i)
-      kst[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_goff[i], kb * KROWB, 0);
+    for (int u = 0; u < K_PER_W; ++u) {
+      const int inst = u * kStagers + wave % kStagers;
+      if (K_INSTR % kStagers == 0 || inst < K_INSTR)
+        buffer_to_lds16(krs, lds + buf * KBUF + inst * kWave * 16, k_goff[u], kb * KROWB);
+    }
+  };
+  auto load_v = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
+    for (int r = 0; r < 4; ++r) {
+      const int off = v_goff + r * KROWB;
       if constexpr (VIN == 16) {
-        vst[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_goff[i], kb * KROWB, 0);
+        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, kb * KROWB, 0);
+        vst[r][0] = x[0]; vst[r][1] = x[1]; vst[r][2] = x[2]; vst[r][3] = x[3];
+      } else if constexpr (VIN == 8) {
+        u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, kb * KROWB, 0);
+        vst[r][0] = x[0]; vst[r][1] = x[1];
       } else {
-        u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(vrs, v_goff[i], kb * KROWB, 0);
-        vst[i] = u32x4{x[0], x[1], 0u, 0u};
+        vst[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, kb * KROWB, 0);
       }
     }
   };
-
-  auto store_block = [&](int buf) {
+  // Convert the 4 x VD block held in registers to fp16 and write its VD rows
+  // of V^T into V buffer buf.
+  auto store_v = [&](int buf) {
+    uint32_t h[4][VD / 2];  // fp16 pairs along d, per key
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i)
-      *reinterpret_cast<u32x4*>(lds + buf * KBUF + k_loff[i]) = kst[i];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      u32x4 h;
-      if constexpr (DT == FA_DTYPE_FP16) {
-        h = vst[i];
-      } else if constexpr (DT == FA_DTYPE_BF16) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) h[w] = v_pair_to_f16<DT, false>(vst[i][w]);
-      } else {
-        h[0] = v_pair_to_f16<DT, false>(vst[i][0]);
-        h[1] = v_pair_to_f16<DT, true>(vst[i][0]);
-        h[2] = v_pair_to_f16<DT, false>(vst[i][1]);
-        h[3] = v_pair_to_f16<DT, true>(vst[i][1]);
+      for (int w = 0; w < VD / 2; ++w) {
+        if constexpr (ES == 2) {
+          h[r][w] = v_pair_to_f16<DT, false>(vst[r][w]);
+        } else if (w & 1) {
+          h[r][w] = v_pair_to_f16<DT, true>(vst[r][w / 2]);
+        } else {
+          h[r][w] = v_pair_to_f16<DT, false>(vst[r][w / 2]);
+        }
       }
-      *reinterpret_cast<u32x4*>(lds + buf * VBUF + v_loff[i]) = h;
+#pragma unroll
+    for (int e = 0; e < VD; ++e) {
+      const int w = e / 2;
+      uint32_t lo, hi;
+      if (e & 1) {
+        lo = (h[0][w] >> 16) | (h[1][w] & 0xffff0000u);
+        hi = (h[2][w] >> 16) | (h[3][w] & 0xffff0000u);
+      } else {
+        lo = (h[0][w] & 0xffffu) | (h[1][w] << 16);
+        hi = (h[2][w] & 0xffffu) | (h[3][w] << 16);
+      }
+      *reinterpret_cast<u32x2*>(lds + buf * VBUF + v_loff + e * VTROW) = u32x2{lo, hi};
     }
   };
+  // Wait for this wave's outstanding global loads (including those writing LDS).
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // ---- per-lane LDS operand addresses (block-independent parts) -------------
   // K (A operand of S^T): row kt*32 + lr, logical chunk(s) of k-step ks.
@@ -349,25 +406,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       const int lc = (ks * E::kstep + hh * (E::kstep / 2)) * ES / 16 + u;
       k_raddr[ks][u] = lr * KROWB + ((lc ^ swz<KROWB>(lr)) * 16);
     }
-  // V (A operand of O^T = V^T P^T) via ds_read_b64_tr_b16.  In each group of
-  // 16 lanes, lane 4e + r reads 4 d-values (4r..4r+3 of the group's 16) of
-  // key K0 + e; the transposed read hands lane i the 4 keys K0..K0+3 at d-value
-  // i.  Group g covers d-values 16*(g%2) .. +15 of a 32-row d tile and keys
-  // 4*(g/2) .. +3 of each 8-key half.
-  int v_raddr[NDT][2];
-  {
-    const int grp = lane >> 4, li = lane & 15;
-    const int e = li >> 2, r = li & 3;
-#pragma unroll
-    for (int t = 0; t < NDT; ++t)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int key = 8 * half + 4 * (grp >> 1) + e;
-        const int d = t * 32 + 16 * (grp & 1) + 4 * r;
-        const int lc = d / 8;
-        v_raddr[t][half] = 2 * KBUF + key * VROWB + ((lc ^ swz<VROWB>(key)) * 16) + (d % 8) * 2;
-      }
-  }
+  // V^T (A operand of O^T = V^T P^T): row t*32 + lr, the 8 contiguous key
+  // positions 16*s + 8*hh .. +7 of key tile kt.
+  const int vt_raddr = 2 * KBUF + lr * VTROW + 16 * hh;
 
   // ---- running softmax state and the O^T accumulator --------------------------
   f32x16 acc[NDT];
@@ -379,22 +420,34 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // <= 2^kRescaleLog2 and O, l are consistent without a rescale.
   float m_run = -INFINITY;
   float l_run = 0.0f;  // this lane's share of the row sum, relative to m_run
+  f32x16 st[2];        // S^T of the block between its MFMA phase and its softmax
+  uint32_t pw[2][2][4];  // P as fp16 pairs, B operand of O^T += V^T P^T
 
-  load_block(0);
-  store_block(0);
-  if (nblk > 1) load_block(kBC);
-  __syncthreads();
+  // A wave whose rows all precede block j has nothing to compute in it.
+  auto active = [&](int j) { return !(CAUSAL && j * kBC > qw0 + kQW - 1); };
 
-  for (int j = 0; j < nblk; ++j) {
-    const int kb = j * kBC;
-    const int buf = j & 1;
-    const uint8_t* kbuf = lds + buf * KBUF;
-    const uint8_t* vbuf = lds + buf * VBUF;
-
-    // A wave whose rows all precede this block has nothing to compute in it.
-    if (!(CAUSAL && kb > qw0 + kQW - 1)) {
-      // S^T = K_j Q^T: two 32-key tiles of this wave's 32 queries.
-      f32x16 st[2];
+  // MFMA phase j: O^T += V^T P^T for block j-1, then S^T = K_j Q^T.
+  auto mfma_phase = [&](int j) {
+    if (j >= 1 && active(j - 1)) {
+      const uint8_t* vbuf = lds + ((j - 1) & 1) * VBUF;
+      // Slot i of lane half hh in k-step s of key tile kt is key
+      // kt*32 + 16*s + 8*(i/4) + 4*hh + (i%4), the order the S^T accumulator
+      // holds, and the order of V^T's permuted key positions 16*s + 8*hh + i.
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(
+                vbuf + vt_raddr + t * 32 * VTROW + (kt * 32 + 16 * s) * 2);
+            u32x4 b = {pw[kt][s][0], pw[kt][s][1], pw[kt][s][2], pw[kt][s][3]};
+            acc[t] = mfma_pv(a, b, acc[t]);
+          }
+      mfma_read_pipeline<NDT * 4, 1, 4>();
+    }
+    if (j < nblk && active(j)) {
+      const uint8_t* kbuf = lds + (j & 1) * KBUF;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         st[kt] = f32x16{};
@@ -410,85 +463,114 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
           st[kt] = mfma_qk<DT>(a, qreg[ks], st[kt]);
         }
       }
+      mfma_read_pipeline<2 * NKS, KCH, (2 * NKS < 4 ? 2 * NKS : 4)>();
+    }
+  };
 
-      // Keys past N, and (causal) keys after the query, are masked out.
-      const bool need_mask = (kb + kBC > N) || (CAUSAL && kb + kBC - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + kt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-            bool keep = key < N;
-            if constexpr (CAUSAL) keep = keep && key <= my_q;
-            st[kt][i] = keep ? st[kt][i] : -INFINITY;
-          }
-      }
-
-      // Block row max (in-lane over 32 keys, then across the lane pair).  The
-      // IEEE maximum builtin lowers to one v_maximum3_f32 per two scores.
-      float mx = st[0][0];
-#pragma unroll
-      for (int i = 1; i < 15; i += 2) mx = vmax(vmax(mx, st[0][i]), st[0][i + 1]);
-      mx = vmax(mx, st[0][15]);
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = vmax(vmax(mx, st[1][i]), st[1][i + 1]);
-      mx = max_pair32(mx);
-
-      // Move the reference max only when some row's block max passed it by
-      // more than the margin (wave-uniform branch).
-      const bool grow = (mx - m_run) * c > kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
-      }
-      const float mc = m_run * c;
-
-      float rs = 0.0f;
-      uint32_t pw[2][2][4];  // [kt][k-step][dword] fp16 pairs: B operand of O^T += V^T P^T
+  // VALU phase j: mask, online softmax of block j (P as fp16, row sum, moving
+  // the reference max and rescaling O^T when needed).
+  auto valu_phase = [&](int j) {
+    if (!active(j)) return;
+    const int kb = j * kBC;
+    if ((kb + kBC > N) || (CAUSAL && kb + kBC - 1 > qw0)) {
+      // Keys past N, and (causal) keys after the query, get score -inf.
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][i], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][i + 1], c, -mc));
-          rs += p0 + p1;
-          pw[kt][i / 8][(i % 8) / 2] = pack_f16x2(p0, p1);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + kt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+          bool keep = key < N;
+          if constexpr (CAUSAL) keep = keep && key <= my_q;
+          st[kt][i] = keep ? st[kt][i] : -INFINITY;
         }
-      l_run += rs;
-
-      // O^T += V^T P^T.  Slot j of lane half hh in k-step s of key tile kt is
-      // key kt*32 + 16*s + 8*(j/4) + 4*hh + (j%4), the order the S^T
-      // accumulator already holds; the transposed V reads follow it.
-#pragma unroll
-      for (int t = 0; t < NDT; ++t)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int krow = (kt * 32 + 16 * s) * VROWB;
-            short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_short4_t*)(vbuf + krow + v_raddr[t][0]));
-            short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_short4_t*)(vbuf + krow + v_raddr[t][1]));
-            u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-            u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-            u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-            u32x4 b = {pw[kt][s][0], pw[kt][s][1], pw[kt][s][2], pw[kt][s][3]};
-            acc[t] = mfma_pv(a, b, acc[t]);
-          }
     }
+    // Block row max: in-lane over 32 keys (one v_maximum3_f32 per two scores),
+    // then across the lane pair.
+    float mx = st[0][0];
+#pragma unroll
+    for (int i = 1; i < 15; i += 2) mx = vmax(vmax(mx, st[0][i]), st[0][i + 1]);
+    mx = vmax(mx, st[0][15]);
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = vmax(vmax(mx, st[1][i]), st[1][i + 1]);
+    mx = max_pair32(mx);
+    const bool rescale = __builtin_amdgcn_ballot_w64((mx - m_run) * c > kRescaleLog2) != 0;
+    const float m_use = rescale ? vmax(m_run, mx) : m_run;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
+    m_run = m_use;
+    // p = exp2(c s - c m): all FMAs, then all exponentials, in place, so the
+    // 32 independent chains overlap instead of waiting on one temporary.
+    const float nmc = -m_use * c;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = fmaf(st[kt][i], c, nmc);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = __builtin_amdgcn_exp2f(st[kt][i]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) pw[kt][i / 8][(i % 8) / 2] = pack_f16x2(st[kt][i], st[kt][i + 1]);
+    // Row sum as a pairwise tree (depth 5 instead of a 32-long chain).
+    float t16[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t16[i] = st[0][i] + st[1][i];
+#pragma unroll
+    for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) t16[i] += t16[i + w];
+    const float rs = t16[0];
+    l_run = l_run * alpha + rs;
+    if (rescale) {
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
+    }
+  };
 
-    // Stage block j+1 into the other buffer (its readers all passed the last
-    // barrier), then start the global loads of block j+2.
-    if (j + 1 < nblk) store_block(buf ^ 1);
-    if (j + 2 < nblk) load_block(kb + 2 * kBC);
+  // ---- ping-pong schedule ------------------------------------------------------
+  // Every wave runs the same sequence: MFMA phase 0, VALU phase 0, MFMA phase
+  // 1, ..., MFMA phase nblk (P V of the last block), one workgroup barrier
+  // after each phase.  Group 1 passes one extra barrier before starting (and
+  // group 0 one after finishing), so group 1 runs one phase behind: on every
+  // SIMD, which holds one wave of each group, one wave's MFMAs overlap the
+  // other wave's softmax.
+  // Group 0 stages the data.  In its MFMA phase j it issues the loads of
+  // K(j+1) and V(j) and waits for them at the end of its VALU phase j, so they
+  // are resident when MFMA phase j+1 begins (K(j) is read in MFMA phase j, V(j)
+  // in MFMA phase j+1, by group 1 one phase later).  With double buffers K(j+1)
+  // and V(j) replace K(j-1) and V(j-2), whose last readers (group 1) finished
+  // before group 0 began MFMA phase j.
+  {
+    constexpr int NZ = (2 * KBUF + 2 * VBUF) / 16;
+    for (int i = tid; i < NZ; i += kThreads)
+      reinterpret_cast<u32x4*>(lds)[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();  // zeros land before any load can write the same bytes
+  }
+  load_k(0, 0);
+  wait_loads();
+  __syncthreads();
+
+  const bool stager = (group == 0);
+  if (group == 1) __syncthreads();
+  for (int j = 0; j <= nblk; ++j) {
+    if (stager) {
+      if (j + 1 < nblk) load_k((j + 1) * kBC, (j + 1) & 1);
+      if (j < nblk) load_v(j * kBC);
+    }
+    mfma_phase(j);
+    __syncthreads();
+    if (j < nblk) {
+      if (stager) {
+        wait_loads();
+        store_v(j & 1);
+      }
+      valu_phase(j);
+    }
+    if (stager) wait_loads();
     __syncthreads();
   }
+  if (group == 0) __syncthreads();
 
   // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
