@@ -43,8 +43,7 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;          // two waves per SIMD, in two groups of four
-constexpr int kGroupWaves = 4;
+constexpr int kWaves = 8;          // two waves per SIMD
 constexpr int kThreads = kWave * kWaves;
 constexpr int kQW = 32;            // query rows per wave
 constexpr int kBR = kQW * kWaves;  // query rows per workgroup
@@ -125,6 +124,25 @@ __device__ __forceinline__ void mfma_read_pipeline() {
     __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
+
+// As above, with VPM VALU instructions placed after every MFMA: the MFMA
+// runs for 32+ cycles while the wave issues independent VALU work.
+template <int NM, int RPM, int LA, int VPM>
+__device__ __forceinline__ void mfma_read_valu_pipeline() {
+  static_assert(LA <= NM, "look-ahead longer than the run");
+  __builtin_amdgcn_sched_group_barrier(0x100, RPM * LA, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < NM - LA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
+  }
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+  }
 }
 
 // Lanes l and l^32 hold the same query.  v_permlane32_swap with both operands
@@ -255,16 +273,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   constexpr int NKS = D / E::kstep;       // QK^T MFMAs per 32x32 score tile
   constexpr int NDT = D / 32;             // 32-row d tiles of O^T
   constexpr int K_INSTR = kBC * KCPR / kWave;  // 64-lane LDS-load instructions per K stage
-  constexpr int VD = D / 16;              // d values per staging thread (4 keys each)
+  constexpr int VD = D / 32;              // d values per staging thread (4 keys each)
   constexpr int VIN = VD * ES;            // input bytes per key row per staging thread
-  static_assert(kBC * D == 4 * VD * kGroupWaves * kWave, "V staging must tile the staging waves");
+  static_assert(kBC * D == 4 * VD * kThreads, "V staging must tile the workgroup");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * KBUF + 2 * VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int group = wave / kGroupWaves;  // 0 runs one phase ahead of 1
   const int lr = lane & 31;   // row/column inside a 32x32 MFMA tile
   const int hh = lane >> 5;   // half of the wave
 
@@ -311,24 +328,22 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   const int nblk = (kv_end + kBC - 1) / kBC;
 
   // ---- staging -----------------------------------------------------------------
-  // The four waves of group 0 stage every block.  K goes global -> LDS directly
-  // (buffer_load ... lds): one instruction fills 64 consecutive 16-byte LDS
-  // slots, lane t slot t; slot s of a stage holds row s / KCPR, physical
-  // chunk s % KCPR, so each lane fetches the logical chunk the swizzle puts
-  // there.  V goes through registers: staging thread (quad, dgrp) loads keys
-  // 4*quad .. +3 at d values dgrp*VD .. +VD-1, converts them to fp16 and
-  // writes VD rows of V^T, 4 keys (8 bytes) each.
-  constexpr int kStagers = kGroupWaves;
-  constexpr int K_PER_W = (K_INSTR + kStagers - 1) / kStagers;
-  const int stid = (wave % kStagers) * kWave + lane;  // staging thread id, 0..255
+  // All eight waves stage.  K goes global -> LDS directly (buffer_load ...
+  // lds): one instruction fills 64 consecutive 16-byte LDS slots, lane t slot
+  // t; slot s of a stage holds row s / KCPR, physical chunk s % KCPR, so each
+  // lane fetches the logical chunk the swizzle puts there.  V goes through
+  // registers: thread (quad, dgrp) loads keys 4*quad .. +3 at d values
+  // dgrp*VD .. +VD-1, converts them to fp16 and writes VD rows of V^T, 4 keys
+  // (8 bytes) each, one iteration later.
+  constexpr int K_PER_W = (K_INSTR + kWaves - 1) / kWaves;
   int k_goff[K_PER_W];
 #pragma unroll
   for (int u = 0; u < K_PER_W; ++u) {
-    const int slot = (u * kStagers + wave % kStagers) * kWave + lane;
+    const int slot = (u * kWaves + wave) * kWave + lane;
     const int row = slot / KCPR, phys = slot % KCPR;
     k_goff[u] = row * KROWB + ((phys ^ swz<KROWB>(row)) * 16);
   }
-  const int vquad = stid % 16, vdgrp = stid / 16;
+  const int vquad = tid % 16, vdgrp = tid / 16;
   const int v_goff = 4 * vquad * KROWB + vdgrp * VIN;
   int v_loff;
   {
@@ -342,8 +357,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   auto load_k = [&](int kb, int buf) {
 #pragma unroll
     for (int u = 0; u < K_PER_W; ++u) {
-      const int inst = u * kStagers + wave % kStagers;
-      if (K_INSTR % kStagers == 0 || inst < K_INSTR)
+      const int inst = u * kWaves + wave;
+      if (K_INSTR % kWaves == 0 || inst < K_INSTR)
         buffer_to_lds16(krs, lds + buf * KBUF + inst * kWave * 16, k_goff[u], kb * KROWB);
     }
   };
@@ -351,14 +366,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int off = v_goff + r * KROWB;
-      if constexpr (VIN == 16) {
-        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, kb * KROWB, 0);
-        vst[r][0] = x[0]; vst[r][1] = x[1]; vst[r][2] = x[2]; vst[r][3] = x[3];
-      } else if constexpr (VIN == 8) {
+      if constexpr (VIN == 8) {
         u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, kb * KROWB, 0);
         vst[r][0] = x[0]; vst[r][1] = x[1];
-      } else {
+      } else if constexpr (VIN == 4) {
         vst[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, kb * KROWB, 0);
+      } else {
+        vst[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vrs, off, kb * KROWB, 0);
       }
     }
   };
@@ -420,85 +434,62 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // <= 2^kRescaleLog2 and O, l are consistent without a rescale.
   float m_run = -INFINITY;
   float l_run = 0.0f;  // this lane's share of the row sum, relative to m_run
-  f32x16 st[2];        // S^T of the block between its MFMA phase and its softmax
   uint32_t pw[2][2][4];  // P as fp16 pairs, B operand of O^T += V^T P^T
 
-  // A wave whose rows all precede block j has nothing to compute in it.
-  auto active = [&](int j) { return !(CAUSAL && j * kBC > qw0 + kQW - 1); };
-
-  // MFMA phase j: O^T += V^T P^T for block j-1, then S^T = K_j Q^T.
-  auto mfma_phase = [&](int j) {
-    if (j >= 1 && active(j - 1)) {
-      const uint8_t* vbuf = lds + ((j - 1) & 1) * VBUF;
-      // Slot i of lane half hh in k-step s of key tile kt is key
-      // kt*32 + 16*s + 8*(i/4) + 4*hh + (i%4), the order the S^T accumulator
-      // holds, and the order of V^T's permuted key positions 16*s + 8*hh + i.
+  // S^T = K Q^T for the block in K buffer kbuf: two 32-key tiles.  The tiles
+  // alternate so consecutive MFMAs are independent.
+  auto qk = [&](const uint8_t* kbuf, f32x16* st) {
+    st[0] = f32x16{};
+    st[1] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < NDT; ++t)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(
-                vbuf + vt_raddr + t * 32 * VTROW + (kt * 32 + 16 * s) * 2);
-            u32x4 b = {pw[kt][s][0], pw[kt][s][1], pw[kt][s][2], pw[kt][s][3]};
-            acc[t] = mfma_pv(a, b, acc[t]);
-          }
-      mfma_read_pipeline<NDT * 4, 1, 4>();
-    }
-    if (j < nblk && active(j)) {
-      const uint8_t* kbuf = lds + (j & 1) * KBUF;
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        st[kt] = f32x16{};
+        QKOperand<DT> a;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          QKOperand<DT> a;
-#pragma unroll
-          for (int u = 0; u < KCH; ++u) {
-            u32x4 x = *reinterpret_cast<const u32x4*>(kbuf + kt * 32 * KROWB + k_raddr[ks][u]);
-            a.w[4 * u + 0] = x[0]; a.w[4 * u + 1] = x[1];
-            a.w[4 * u + 2] = x[2]; a.w[4 * u + 3] = x[3];
-          }
-          st[kt] = mfma_qk<DT>(a, qreg[ks], st[kt]);
+        for (int u = 0; u < KCH; ++u) {
+          u32x4 x = *reinterpret_cast<const u32x4*>(kbuf + kt * 32 * KROWB + k_raddr[ks][u]);
+          a.w[4 * u + 0] = x[0]; a.w[4 * u + 1] = x[1];
+          a.w[4 * u + 2] = x[2]; a.w[4 * u + 3] = x[3];
         }
+        st[kt] = mfma_qk<DT>(a, qreg[ks], st[kt]);
       }
-      mfma_read_pipeline<2 * NKS, KCH, (2 * NKS < 4 ? 2 * NKS : 4)>();
-    }
   };
 
-  // VALU phase j: mask, online softmax of block j (P as fp16, row sum, moving
-  // the reference max and rescaling O^T when needed).
-  auto valu_phase = [&](int j) {
-    if (!active(j)) return;
-    const int kb = j * kBC;
-    if ((kb + kBC > N) || (CAUSAL && kb + kBC - 1 > qw0)) {
-      // Keys past N, and (causal) keys after the query, get score -inf.
+  // Keys past N, and (causal) keys after the query, get score -inf.  A block
+  // with every key masked for this lane leaves m_run, l_run unchanged and
+  // contributes P = 0 (block 0 always holds a valid key for every row).
+  auto needs_mask = [&](int j) {
+    return (j * kBC + kBC > N) || (CAUSAL && j * kBC + kBC - 1 > qw0);
+  };
+  auto mask = [&](f32x16* st, int kb) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + kt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-          bool keep = key < N;
-          if constexpr (CAUSAL) keep = keep && key <= my_q;
-          st[kt][i] = keep ? st[kt][i] : -INFINITY;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + kt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+        bool keep = key < N;
+        if constexpr (CAUSAL) keep = keep && key <= my_q;
+        st[kt][i] = keep ? st[kt][i] : -INFINITY;
+      }
+  };
+
+  // Online softmax of one block: new reference max (branch-free select),
+  // P as fp16 pairs laid out as the B operand of O^T += V^T P^T, row-sum
+  // update.  Returns the factor O^T must be scaled by when `rescale`.
+  auto softmax = [&](f32x16* st, bool& rescale) -> float {
+    float m0 = st[0][0], m1 = st[1][0];  // two independent chains
+#pragma unroll
+    for (int i = 1; i < 15; i += 2) {
+      m0 = vmax(vmax(m0, st[0][i]), st[0][i + 1]);
+      m1 = vmax(vmax(m1, st[1][i]), st[1][i + 1]);
     }
-    // Block row max: in-lane over 32 keys (one v_maximum3_f32 per two scores),
-    // then across the lane pair.
-    float mx = st[0][0];
-#pragma unroll
-    for (int i = 1; i < 15; i += 2) mx = vmax(vmax(mx, st[0][i]), st[0][i + 1]);
-    mx = vmax(mx, st[0][15]);
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = vmax(vmax(mx, st[1][i]), st[1][i + 1]);
-    mx = max_pair32(mx);
-    const bool rescale = __builtin_amdgcn_ballot_w64((mx - m_run) * c > kRescaleLog2) != 0;
+    const float mx = max_pair32(vmax(vmax(m0, st[0][15]), vmax(m1, st[1][15])));
+    rescale = __builtin_amdgcn_ballot_w64((mx - m_run) * c > kRescaleLog2) != 0;
     const float m_use = rescale ? vmax(m_run, mx) : m_run;
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
     m_run = m_use;
-    // p = exp2(c s - c m): all FMAs, then all exponentials, in place, so the
-    // 32 independent chains overlap instead of waiting on one temporary.
+    // p = exp2(c s - c m): all FMAs, then all exponentials, in place.
     const float nmc = -m_use * c;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -520,27 +511,39 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     for (int w = 8; w >= 1; w /= 2)
 #pragma unroll
       for (int i = 0; i < w; ++i) t16[i] += t16[i + w];
-    const float rs = t16[0];
-    l_run = l_run * alpha + rs;
-    if (rescale) {
-#pragma unroll
-      for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
-    }
+    l_run = l_run * alpha + t16[0];
+    return alpha;
   };
 
-  // ---- ping-pong schedule ------------------------------------------------------
-  // Every wave runs the same sequence: MFMA phase 0, VALU phase 0, MFMA phase
-  // 1, ..., MFMA phase nblk (P V of the last block), one workgroup barrier
-  // after each phase.  Group 1 passes one extra barrier before starting (and
-  // group 0 one after finishing), so group 1 runs one phase behind: on every
-  // SIMD, which holds one wave of each group, one wave's MFMAs overlap the
-  // other wave's softmax.
-  // Group 0 stages the data.  In its MFMA phase j it issues the loads of
-  // K(j+1) and V(j) and waits for them at the end of its VALU phase j, so they
-  // are resident when MFMA phase j+1 begins (K(j) is read in MFMA phase j, V(j)
-  // in MFMA phase j+1, by group 1 one phase later).  With double buffers K(j+1)
-  // and V(j) replace K(j-1) and V(j-2), whose last readers (group 1) finished
-  // before group 0 began MFMA phase j.
+  // O^T += V^T P^T for the block in V buffer vbuf.  Slot i of lane half hh
+  // in k-step s of key tile kt is key kt*32 + 16*s + 8*(i/4) + 4*hh + (i%4),
+  // the order the S^T accumulator holds and the order of V^T's permuted key
+  // positions 16*s + 8*hh + i.  d tiles innermost: consecutive MFMAs update
+  // different accumulators.
+  auto pv = [&](const uint8_t* vbuf) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(
+              vbuf + vt_raddr + t * 32 * VTROW + (kt * 32 + 16 * s) * 2);
+          u32x4 b = {pw[kt][s][0], pw[kt][s][1], pw[kt][s][2], pw[kt][s][3]};
+          acc[t] = mfma_pv(a, b, acc[t]);
+        }
+  };
+
+  // ---- software pipeline ---------------------------------------------------------
+  // Iteration j: the QK^T MFMAs of block j+1 (K buffer (j+1)&1) issue between
+  // the softmax instructions of block j, then P V of block j (V buffer j&1)
+  // runs while V(j+1) is transposed into V buffer (j+1)&1 and the loads of
+  // K(j+2) (into K buffer j&1) and V(j+2) (into registers) go out.  Both
+  // buffers written in iteration j were last read in iteration j-1; one
+  // barrier per iteration.  Two waves share each SIMD, so one wave's MFMAs
+  // also cover the other's VALU work.  In the last iteration the QK^T of the
+  // non-existent block j+1 reads a stale buffer and its result is discarded:
+  // that keeps the loop body free of branches around the MFMAs.
   {
     constexpr int NZ = (2 * KBUF + 2 * VBUF) / 16;
     for (int i = tid; i < NZ; i += kThreads)
@@ -548,29 +551,47 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     __syncthreads();  // zeros land before any load can write the same bytes
   }
   load_k(0, 0);
+  if (nblk > 1) load_k(kBC, 1);
+  load_v(0);
+  wait_loads();
+  store_v(0);
+  if (nblk > 1) load_v(kBC);
   wait_loads();
   __syncthreads();
 
-  const bool stager = (group == 0);
-  if (group == 1) __syncthreads();
-  for (int j = 0; j <= nblk; ++j) {
-    if (stager) {
-      if (j + 1 < nblk) load_k((j + 1) * kBC, (j + 1) & 1);
-      if (j < nblk) load_v(j * kBC);
+  f32x16 sa[2], sb[2];
+  qk(lds, sa);
+  __syncthreads();  // iteration 0 overwrites K buffer 0 with K(2)
+
+  auto step = [&](int j, f32x16* s_cur, f32x16* s_next) {
+    const int buf = j & 1;
+    if (needs_mask(j)) mask(s_cur, j * kBC);
+    // QK^T(j+1) interleaved with softmax(j).
+    qk(lds + (buf ^ 1) * KBUF, s_next);
+    bool rescale;
+    const float alpha = softmax(s_cur, rescale);
+    mfma_read_valu_pipeline<2 * NKS, KCH, (2 * NKS < 4 ? 2 * NKS : 4), 8>();
+    if (rescale) {
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
     }
-    mfma_phase(j);
-    __syncthreads();
-    if (j < nblk) {
-      if (stager) {
-        wait_loads();
-        store_v(j & 1);
-      }
-      valu_phase(j);
+    // Staging, then P V of block j.
+    if (j + 1 < nblk) store_v(buf ^ 1);      // V(j+1), loaded last iteration
+    if (j + 2 < nblk) {
+      load_k((j + 2) * kBC, buf);
+      load_v((j + 2) * kBC);
     }
-    if (stager) wait_loads();
+    pv(lds + buf * VBUF);
+    mfma_read_pipeline<NDT * 4, 1, (NDT * 4 < 8 ? NDT * 4 : 8)>();
+    wait_loads();
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < nblk; j += 2) {
+    step(j, sa, sb);
+    step(j + 1, sb, sa);
   }
-  if (group == 0) __syncthreads();
+  if (j < nblk) step(j, sa, sb);
 
   // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
