@@ -10,29 +10,34 @@
 //
 // gfx950 mapping (the pages' TMA / mbarrier / WGMMA / TMEM machinery has no
 // counterpart here and is not imitated):
-//   * workgroup = 4 waves of 64 lanes; each wave owns 32 query rows, so a
-//     workgroup covers BR = 128 rows of one (b, h) head;
-//   * K/V blocks of BC = 64 keys go global -> VGPR -> LDS through buffer
-//     loads (a per-head buffer resource returns zeros past row N, so ragged
-//     tails need no bounds branches); LDS is double-buffered, one barrier per
-//     block, and the global loads of block j+2 are in flight while block j is
-//     computed;
+//   * workgroup = 8 waves of 64 lanes, two per SIMD; each wave owns 32 query
+//     rows, so a workgroup covers BR = 256 rows of one (b, h) head and the
+//     whole K/V sequence streams past it in blocks of BC = 64 keys;
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{f16,bf16} (or the fp8 v_mfma_scale_f32_32x32x64
-//     with unit block scales).  In the 32x32 accumulator layout a lane owns
-//     one column (= one query) and 16 rows (= keys), so the row max / row sum
-//     of the softmax are in-lane reductions plus one exchange with the lane
-//     32 apart (v_permlane32_swap);
+//     with unit block scales), Q held in registers as the B operand.  In the
+//     32x32 accumulator layout a lane owns one column (= one query) and 16
+//     rows (= keys), so the row max / row sum of the softmax are in-lane
+//     reductions plus one exchange with the lane 32 apart (v_permlane32_swap);
 //   * the same accumulator registers, rounded to fp16, are already the B
 //     operand of O^T += V^T P^T: the key order inside one MFMA's contraction
 //     is free, so P never moves between lanes or through LDS;
-//   * V stays row-major in LDS (converted to fp16 for bf16 / fp8 inputs on
-//     the way in); ds_read_b64_tr_b16 delivers the transposed V^T operand;
-//   * LDS rows carry an XOR swizzle of their 16-byte chunks so the operand
-//     reads are free of bank conflicts without padding;
+//   * K goes global -> LDS directly (buffer_load ... lds) into rows whose
+//     16-byte chunks carry an XOR swizzle, so the operand reads are free of
+//     bank conflicts; V goes through registers, is converted to fp16 and
+//     stored transposed (V^T rows, keys permuted inside groups of 16) so each
+//     P V operand is one ds_read_b128;
+//   * per-head buffer resources return zeros past row N, so ragged tails need
+//     no bounds branches (keys past N are masked to -inf in the scores);
+//   * software pipeline: iteration j issues the loads of K(j+2) and V(j+1)
+//     and, in one run of MFMAs, P V of block j-1 followed by QK^T of block
+//     j+1, with the softmax of block j and the V^T store of block j placed
+//     between the MFMAs; one workgroup barrier per block;
 //   * the reference max of a row only moves when a block max exceeds it by
 //     more than 2^8, so the O rescale is skipped for almost every block
-//     (probabilities then stay <= 2^8 and O, l remain consistent).
+//     (probabilities then stay <= 2^8 and O, l remain consistent);
+//   * workgroups are mapped to XCDs by head so the query tiles of a head,
+//     which all read the same K and V, share one L2.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -142,6 +147,31 @@ __device__ __forceinline__ void mfma_read_valu_pipeline() {
   for (int i = 0; i < LA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+  }
+}
+
+// One run of NA MFMAs fed by RA LDS reads each, then NB MFMAs fed by RB
+// reads each.  The reads run LA MFMAs ahead; after every MFMA come VPM VALU
+// instructions and TPM transcendental ones (v_exp_f32 and the like form a
+// class of their own for the scheduler); after MFMAs 3 .. 3+NW-1 one LDS
+// write each, and after MFMAs
+// 5 .. 5+NVM-1 one global load each, so the staging of the next block hides
+// behind the matrix work too.
+template <int NA, int RA, int NB, int RB, int LA, int VPM, int TPM, int NW, int NVM, int I = 0>
+__device__ __forceinline__ void mfma_run_pipeline() {
+  constexpr int NM = NA + NB;
+  static_assert(LA <= NM && 5 + NVM <= NM, "run too short");
+  if constexpr (I == 0)  // reads of the first LA MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, LA <= NA ? LA * RA : NA * RA + (LA - NA) * RB, 0);
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA I
+    if constexpr (I + LA < NM)
+      __builtin_amdgcn_sched_group_barrier(0x100, I + LA < NA ? RA : RB, 0);  // reads of I+LA
+    if constexpr (I >= 3 && I < 3 + NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if constexpr (I >= 5 && I < 5 + NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x400, TPM, 0);  // transcendental
+    mfma_run_pipeline<NA, RA, NB, RB, LA, VPM, TPM, NW, NVM, I + 1>();
   }
 }
 
@@ -277,7 +307,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   constexpr int VIN = VD * ES;            // input bytes per key row per staging thread
   static_assert(kBC * D == 4 * VD * kThreads, "V staging must tile the workgroup");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * KBUF + 2 * VBUF];
+  // Two K stages and two V^T stages, each an array of its own: the compiler
+  // can then tell the buffers being filled from the ones being read and
+  // interleave the staging with the MFMA run.
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds1[KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds0[VBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds1[VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -334,7 +370,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // lane fetches the logical chunk the swizzle puts there.  V goes through
   // registers: thread (quad, dgrp) loads keys 4*quad .. +3 at d values
   // dgrp*VD .. +VD-1, converts them to fp16 and writes VD rows of V^T, 4 keys
-  // (8 bytes) each, one iteration later.
+  // (8 bytes) each, one iteration later.  Block offsets go into the VGPR
+  // offset, which the buffer range check covers: rows at or past N read 0.
+  // Blocks past the last one this workgroup needs are pointed beyond every
+  // head's range, so they read 0 without touching memory.
   constexpr int K_PER_W = (K_INSTR + kWaves - 1) / kWaves;
   int k_goff[K_PER_W];
 #pragma unroll
@@ -349,36 +388,41 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   {
     const int qq = vquad % 4;  // quad inside its 16-key group -> position quad
     const int keypos = 16 * (vquad / 4) + 4 * ((qq >> 1) + 2 * (qq & 1));
-    v_loff = 2 * KBUF + vdgrp * VD * VTROW + keypos * 2;
+    v_loff = vdgrp * VD * VTROW + keypos * 2;
   }
   constexpr int VW = (VIN + 3) / 4;  // dwords of one key row of a staging thread
   uint32_t vst[4][VW];
+  // Byte offset of key row kb, or one past every valid offset (N * KROWB is
+  // at most 2^30) for a block the workgroup does not use.
+  auto block_off = [&](int kb) { return kb < kv_end ? kb * KROWB : (1 << 30); };
 
-  auto load_k = [&](int kb, int buf) {
+  auto load_k = [&](int kb, uint8_t* kbuf) {
+    const int boff = block_off(kb);
 #pragma unroll
     for (int u = 0; u < K_PER_W; ++u) {
       const int inst = u * kWaves + wave;
       if (K_INSTR % kWaves == 0 || inst < K_INSTR)
-        buffer_to_lds16(krs, lds + buf * KBUF + inst * kWave * 16, k_goff[u], kb * KROWB);
+        buffer_to_lds16(krs, kbuf + inst * kWave * 16, k_goff[u] + boff, 0);
     }
   };
   auto load_v = [&](int kb) {
+    const int boff = block_off(kb);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int off = v_goff + r * KROWB;
+      const int off = v_goff + r * KROWB + boff;
       if constexpr (VIN == 8) {
-        u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, kb * KROWB, 0);
+        u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, 0);
         vst[r][0] = x[0]; vst[r][1] = x[1];
       } else if constexpr (VIN == 4) {
-        vst[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, kb * KROWB, 0);
+        vst[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, 0);
       } else {
-        vst[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vrs, off, kb * KROWB, 0);
+        vst[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0);
       }
     }
   };
   // Convert the 4 x VD block held in registers to fp16 and write its VD rows
-  // of V^T into V buffer buf.
-  auto store_v = [&](int buf) {
+  // of V^T into the V^T buffer vbuf.
+  auto store_v = [&](uint8_t* vbuf) {
     uint32_t h[4][VD / 2];  // fp16 pairs along d, per key
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -403,11 +447,14 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
         lo = (h[0][w] & 0xffffu) | (h[1][w] << 16);
         hi = (h[2][w] & 0xffffu) | (h[3][w] << 16);
       }
-      *reinterpret_cast<u32x2*>(lds + buf * VBUF + v_loff + e * VTROW) = u32x2{lo, hi};
+      *reinterpret_cast<u32x2*>(vbuf + v_loff + e * VTROW) = u32x2{lo, hi};
     }
   };
-  // Wait for this wave's outstanding global loads (including those writing LDS).
-  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // Workgroup barrier that leaves global loads in flight: this wave's LDS
+  // accesses complete, then s_barrier.  (__syncthreads would also wait for
+  // every outstanding global load.)  Loads that must have landed before it
+  // are waited for explicitly with vmcnt.
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   // ---- per-lane LDS operand addresses (block-independent parts) -------------
   // K (A operand of S^T): row kt*32 + lr, logical chunk(s) of k-step ks.
@@ -422,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     }
   // V^T (A operand of O^T = V^T P^T): row t*32 + lr, the 8 contiguous key
   // positions 16*s + 8*hh .. +7 of key tile kt.
-  const int vt_raddr = 2 * KBUF + lr * VTROW + 16 * hh;
+  const int vt_raddr = lr * VTROW + 16 * hh;
 
   // ---- running softmax state and the O^T accumulator --------------------------
   f32x16 acc[NDT];
@@ -434,7 +481,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // <= 2^kRescaleLog2 and O, l are consistent without a rescale.
   float m_run = -INFINITY;
   float l_run = 0.0f;  // this lane's share of the row sum, relative to m_run
-  uint32_t pw[2][2][4];  // P as fp16 pairs, B operand of O^T += V^T P^T
+  // P as fp16 pairs, the B operand of O^T += V^T P^T: [key tile][k-step][dword].
+  typedef uint32_t PRegs[2][2][4];
 
   // S^T = K Q^T for the block in K buffer kbuf: two 32-key tiles.  The tiles
   // alternate so consecutive MFMAs are independent.
@@ -477,7 +525,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // Online softmax of one block: new reference max (branch-free select),
   // P as fp16 pairs laid out as the B operand of O^T += V^T P^T, row-sum
   // update.  Returns the factor O^T must be scaled by when `rescale`.
-  auto softmax = [&](f32x16* st, bool& rescale) -> float {
+  auto softmax = [&](f32x16* st, PRegs& pw, bool& rescale) -> float {
     float m0 = st[0][0], m1 = st[1][0];  // two independent chains
 #pragma unroll
     for (int i = 1; i < 15; i += 2) {
@@ -520,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // the order the S^T accumulator holds and the order of V^T's permuted key
   // positions 16*s + 8*hh + i.  d tiles innermost: consecutive MFMAs update
   // different accumulators.
-  auto pv = [&](const uint8_t* vbuf) {
+  auto pv = [&](const uint8_t* vbuf, const PRegs& pw) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -535,63 +583,81 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   };
 
   // ---- software pipeline ---------------------------------------------------------
-  // Iteration j: the QK^T MFMAs of block j+1 (K buffer (j+1)&1) issue between
-  // the softmax instructions of block j, then P V of block j (V buffer j&1)
-  // runs while V(j+1) is transposed into V buffer (j+1)&1 and the loads of
-  // K(j+2) (into K buffer j&1) and V(j+2) (into registers) go out.  Both
-  // buffers written in iteration j were last read in iteration j-1; one
-  // barrier per iteration.  Two waves share each SIMD, so one wave's MFMAs
-  // also cover the other's VALU work.  In the last iteration the QK^T of the
-  // non-existent block j+1 reads a stale buffer and its result is discarded:
-  // that keeps the loop body free of branches around the MFMAs.
-  {
-    constexpr int NZ = (2 * KBUF + 2 * VBUF) / 16;
-    for (int i = tid; i < NZ; i += kThreads)
-      reinterpret_cast<u32x4*>(lds)[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();  // zeros land before any load can write the same bytes
+  // Iteration j fills K buffer j&1 with K(j+2) (that buffer held K(j), read
+  // in iteration j-1), writes V(j) -- loaded into registers during iteration
+  // j-1 -- to V^T buffer j&1 (last read in iteration j-1) and loads V(j+1)
+  // into those registers.  One run of MFMAs, P V of block j-1 (V^T buffer
+  // (j-1)&1, P(j-1) kept from the previous iteration) followed by QK^T of
+  // block j+1 (K buffer (j+1)&1), carries the staging and the softmax of
+  // block j in the issue slots between the MFMAs.  Each wave then waits for
+  // its own loads and the workgroup meets at one barrier.  Loads are issued
+  // unconditionally (blocks past the end read 0), so the loop body is a
+  // straight line; the QK^T of the block after the last is computed and
+  // discarded, and iteration 0 multiplies a zero P(-1) with the zeroed
+  // V^T buffer 1.
+  for (int i = tid; i < VBUF / 16; i += kThreads) {
+    reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  load_k(0, 0);
-  if (nblk > 1) load_k(kBC, 1);
+  load_k(0, k_lds0);
+  load_k(kBC, k_lds1);
   load_v(0);
-  wait_loads();
-  store_v(0);
-  if (nblk > 1) load_v(kBC);
-  wait_loads();
-  __syncthreads();
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // this wave's K(0), K(1); V(0) may fly
+  barrier();
 
   f32x16 sa[2], sb[2];
-  qk(lds, sa);
-  __syncthreads();  // iteration 0 overwrites K buffer 0 with K(2)
+  PRegs pa, pb = {};
+  qk(k_lds0, sa);
+  barrier();  // iteration 0 overwrites K buffer 0 with K(2)
 
-  auto step = [&](int j, f32x16* s_cur, f32x16* s_next) {
-    const int buf = j & 1;
+  constexpr int NPV = NDT * 4;     // P V MFMAs per block
+  constexpr int NQK = 2 * NKS;     // QK^T MFMAs per block
+  constexpr int VPM = (160 + NPV + NQK - 1) / (NPV + NQK);  // about 160 VALU per block
+  constexpr int TPM = (kBC / 2 + NPV + NQK) / (NPV + NQK);  // kBC / 2 + 1 exponentials per block
+  constexpr int NVM = K_PER_W + 4;                          // global loads per wave
+  auto step = [&](int j, uint8_t* k_next, uint8_t* k_fill, const uint8_t* v_prev,
+                  uint8_t* v_fill, f32x16* s_cur, f32x16* s_next, PRegs& p_cur,
+                  const PRegs& p_prev) {
     if (needs_mask(j)) mask(s_cur, j * kBC);
-    // QK^T(j+1) interleaved with softmax(j).
-    qk(lds + (buf ^ 1) * KBUF, s_next);
+    load_k((j + 2) * kBC, k_fill);  // K(j+2)
+    store_v(v_fill);                // V(j) -> V^T
+    load_v((j + 1) * kBC);          // V(j+1) -> registers
+    pv(v_prev, p_prev);             // P V of block j-1
+    qk(k_next, s_next);             // QK^T of block j+1
     bool rescale;
-    const float alpha = softmax(s_cur, rescale);
-    mfma_read_valu_pipeline<2 * NKS, KCH, (2 * NKS < 4 ? 2 * NKS : 4), 8>();
-    if (rescale) {
+    const float alpha = softmax(s_cur, p_cur, rescale);
+    mfma_run_pipeline<NPV, 1, NQK, KCH, 4, VPM, TPM, VD / 2, NVM>();
+    // Keep the softmax in this block, beside the MFMAs: its results are only
+    // used next iteration, and the compiler would otherwise sink it there.
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) asm volatile("" ::"v"(p_cur[kt][s][w]));
+    asm volatile("" ::"v"(l_run));
+    if (rescale) {  // after P V(j-1): all of O^T is relative to the old max
 #pragma unroll
       for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
     }
-    // Staging, then P V of block j.
-    if (j + 1 < nblk) store_v(buf ^ 1);      // V(j+1), loaded last iteration
-    if (j + 2 < nblk) {
-      load_k((j + 2) * kBC, buf);
-      load_v((j + 2) * kBC);
-    }
-    pv(lds + buf * VBUF);
-    mfma_read_pipeline<NDT * 4, 1, (NDT * 4 < 8 ? NDT * 4 : 8)>();
-    wait_loads();
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();
+  };
+  auto last_pv = [&](const uint8_t* vbuf, const PRegs& p_last) {
+    pv(vbuf, p_last);
+    mfma_read_pipeline<NPV, 1, (NPV < 8 ? NPV : 8)>();
   };
   int j = 0;
   for (; j + 1 < nblk; j += 2) {
-    step(j, sa, sb);
-    step(j + 1, sb, sa);
+    step(j, k_lds1, k_lds0, v_lds1, v_lds0, sa, sb, pa, pb);
+    step(j + 1, k_lds0, k_lds1, v_lds0, v_lds1, sb, sa, pb, pa);
   }
-  if (j < nblk) step(j, sa, sb);
+  if (j < nblk) {
+    step(j, k_lds1, k_lds0, v_lds1, v_lds0, sa, sb, pa, pb);
+    last_pv(v_lds0, pa);  // block nblk-1 = j is even
+  } else {
+    last_pv(v_lds1, pb);  // block nblk-1 = j-1 is odd
+  }
 
   // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
