@@ -436,17 +436,14 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
           h[r][w] = v_pair_to_f16<DT, false>(vst[r][w / 2]);
         }
       }
+    // v_perm_b32 picks bytes of {a, b} (b = bytes 0-3, a = bytes 4-7): the
+    // low halves of two keys for an even d, the high halves for an odd one.
 #pragma unroll
     for (int e = 0; e < VD; ++e) {
       const int w = e / 2;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (h[0][w] >> 16) | (h[1][w] & 0xffff0000u);
-        hi = (h[2][w] >> 16) | (h[3][w] & 0xffff0000u);
-      } else {
-        lo = (h[0][w] & 0xffffu) | (h[1][w] << 16);
-        hi = (h[2][w] & 0xffffu) | (h[3][w] << 16);
-      }
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(h[1][w], h[0][w], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(h[3][w], h[2][w], sel);
       *reinterpret_cast<u32x2*>(vbuf + v_loff + e * VTROW) = u32x2{lo, hi};
     }
   };
@@ -551,15 +548,20 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) pw[kt][i / 8][(i % 8) / 2] = pack_f16x2(st[kt][i], st[kt][i + 1]);
-    // Row sum as a pairwise tree (depth 5 instead of a 32-long chain).
-    float t16[16];
+    // Row sum of the fp16 probabilities that multiply V (so numerator and
+    // denominator see the same rounding), two at a time with v_dot2_f32_f16
+    // against (1, 1) in four independent chains.
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t16[i] = st[0][i] + st[1][i];
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int w = 8; w >= 1; w /= 2)
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int i = 0; i < w; ++i) t16[i] += t16[i + w];
-    l_run = l_run * alpha + t16[0];
+        for (int w = 0; w < 4; ++w)
+          part[w] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[kt][s][w]), ones, part[w],
+                                           false);
+    l_run = l_run * alpha + ((part[0] + part[1]) + (part[2] + part[3]));
     return alpha;
   };
 
