@@ -9,6 +9,8 @@ Prints one JSON line:
   value     counted TFLOPS = 4*B*H*N^2*d (halved if causal) / time per step
   roofline  the kernel against the MI355X dense MFMA peak of its input type,
             timed with HIP events on the stream the kernel is launched on
+  clock     the graphics clock read from sysfs while the kernel runs back to
+            back, and the fraction of the dense peak scaled to that clock
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -30,8 +32,10 @@ DEFAULT_WORKLOAD = "fp16_b2h16_n4096_d128"
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The package power limit settles the clock only after a few tenths of a
+    # second of sustained load: warm up for ~0.6 s, then time ~0.3 s.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="workload name (attention_forward_fa_amd.inputs.CONFIGS)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -60,8 +64,58 @@ def copy_calibration(mib, steps):
     return 0
 
 
-def time_gpu(inp, steps, warmup):
-    """Average seconds per fa_fwd call, HIP events on the launch stream."""
+class ClockSampler:
+    """Samples the GPU's graphics clock from sysfs (pp_dpm_sclk, the level
+    marked '*') while the kernel runs back to back.  No single readable
+    pp_dpm_sclk (no GPU, several GPUs) -> no samples."""
+
+    def __init__(self):
+        import glob
+        paths = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+        self.path = paths[0] if len(paths) == 1 else None
+        self.samples, self.mhz = [], None
+
+    def read(self):
+        for line in open(self.path, encoding="ascii"):
+            if line.rstrip().endswith("*"):
+                return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        return None
+
+    def run(self, launch, seconds):
+        """Calls launch() repeatedly for about `seconds`, sampling the clock;
+        returns the mean over the second half (the reading ramps up first)."""
+        import threading
+        import torch
+        if self.path is None:
+            return None
+        stop = threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    c = self.read()
+                except (OSError, ValueError, IndexError):
+                    c = None
+                if c:
+                    self.samples.append(c)
+                time.sleep(0.01)
+
+        t = threading.Thread(target=sample)
+        t.start()
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                launch()
+            torch.cuda.synchronize()
+        stop.set()
+        t.join()
+        s = self.samples[len(self.samples) // 2:]
+        return sum(s) / len(s) if s else None
+
+
+def time_gpu(inp, steps, warmup, clock=None):
+    """Average seconds per fa_fwd call, HIP events on the launch stream; with a
+    ClockSampler, afterwards the mean graphics clock under the same load."""
     import torch
 
     from attention_forward_fa_amd import binding
@@ -87,7 +141,10 @@ def time_gpu(inp, steps, warmup):
         step()
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3 / steps
+    sec = start.elapsed_time(end) * 1e-3 / steps
+    if clock is not None:
+        clock.mhz = clock.run(step, 1.0)
+    return sec
 
 
 def cpu_baseline(inp, budget_s):
@@ -167,7 +224,8 @@ def main(argv=None):
         return copy_calibration(args.copy_calibration, args.steps)
     name, B, H, N, d, dtype, causal, seed = inputs.config(args.workload)
     inp = inputs.draw(B, H, N, d, dtype, causal, seed)
-    sec = time_gpu(inp, args.steps, args.warmup)
+    clock = ClockSampler()
+    sec = time_gpu(inp, args.steps, args.warmup, clock)
     flops, tf, peak = describe(inp, sec)
     if args.sweep:
         for cfg in inputs.CONFIGS:
@@ -197,6 +255,12 @@ def main(argv=None):
                      "unit": "TFLOP/s", "frac": round(tf / peak, 4),
                      "traffic": measured_traffic(name)},
         "frac_of_peak": round(tf / peak, 4),
+        # The dense peak assumes the 2400 MHz top clock; under this load the
+        # package power limit holds the clock lower.  Same work, measured clock:
+        "clock": {"sclk_mhz": round(clock.mhz, 1) if clock.mhz else None,
+                  "peak_at_sclk": round(peak * clock.mhz / 2400.0, 1) if clock.mhz else None,
+                  "frac_at_sclk": round(tf / (peak * clock.mhz / 2400.0), 4) if clock.mhz else None,
+                  "samples": len(clock.samples)},
         "algorithmic_bytes": acc.algorithmic_bytes(B, H, N, d, dtype),
     }
     if not args.no_cpu_baseline:
