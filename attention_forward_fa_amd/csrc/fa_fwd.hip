@@ -10,9 +10,11 @@
 //
 // gfx950 mapping (the pages' TMA / mbarrier / WGMMA / TMEM machinery has no
 // counterpart here and is not imitated):
-//   * workgroup = 8 waves of 64 lanes, two per SIMD; each wave owns 32 query
-//     rows, so a workgroup covers BR = 256 rows of one (b, h) head and the
-//     whole K/V sequence streams past it in blocks of BC = 64 keys;
+//   * each wave of 64 lanes owns 32 query rows; a workgroup of 8 waves
+//     (fp16 / bf16, d = 128: one workgroup per CU) or 4 waves (d = 64, fp8:
+//     two workgroups per CU) covers BR = 256 or 128 rows of one (b, h) head,
+//     two waves per SIMD either way, and the whole K/V sequence streams past
+//     it in blocks of BC = 64 keys;
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{f16,bf16} (or the fp8 v_mfma_scale_f32_32x32x64
 //     with unit block scales), Q held in registers as the B operand.  In the
@@ -48,10 +50,7 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;          // two waves per SIMD
-constexpr int kThreads = kWave * kWaves;
 constexpr int kQW = 32;            // query rows per wave
-constexpr int kBR = kQW * kWaves;  // query rows per workgroup
 constexpr int kBC = 64;            // keys per K/V block
 // The reference max of a row moves only when a block max passes it by more
 // than this many powers of two, bounding every probability by 2^8 (fine for
@@ -82,6 +81,18 @@ template <int DT>
 struct QKOperand {
   uint32_t w[Elem<DT>::opnd_dwords];
 };
+
+// Waves per workgroup, two per SIMD either way.  Eight (one workgroup per CU)
+// where a block carries 32 MFMAs per wave (fp16 / bf16 at d = 128); four (two
+// workgroups per CU, which drift apart and fill each other's barrier waits)
+// where a block has fewer MFMAs per softmax instruction (d = 64, fp8).
+template <int DT, int D>
+struct Shape {
+  static constexpr int waves = (D == 128 && DT != FA_DTYPE_FP8_E4M3) ? 8 : 4;
+  static constexpr int threads = kWave * waves;
+  static constexpr int br = kQW * waves;  // query rows per workgroup
+};
+constexpr int kMinBR = kQW * 4;           // smallest query tile of any kernel
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma_qk(const QKOperand<DT>& a, const QKOperand<DT>& b,
@@ -287,8 +298,11 @@ __device__ __forceinline__ void tile_of(int w, int n_heads, int n_tiles, bool ca
 }
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
+__global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Params p) {
   using E = Elem<DT>;
+  constexpr int kWaves = Shape<DT, D>::waves;
+  constexpr int kThreads = Shape<DT, D>::threads;
+  constexpr int kBR = Shape<DT, D>::br;
   constexpr int ES = E::bytes;
   constexpr int KROWB = D * ES;           // bytes per K row, global and LDS
   constexpr int KCPR = KROWB / 16;        // 16-byte chunks per K row
@@ -303,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   constexpr int NKS = D / E::kstep;       // QK^T MFMAs per 32x32 score tile
   constexpr int NDT = D / 32;             // 32-row d tiles of O^T
   constexpr int K_INSTR = kBC * KCPR / kWave;  // 64-lane LDS-load instructions per K stage
-  constexpr int VD = D / 32;              // d values per staging thread (4 keys each)
+  constexpr int VD = kBC * D / (4 * kThreads);  // d values per staging thread (4 keys each)
   constexpr int VIN = VD * ES;            // input bytes per key row per staging thread
   static_assert(kBC * D == 4 * VD * kThreads, "V staging must tile the workgroup");
 
@@ -410,7 +424,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int off = v_goff + r * KROWB + boff;
-      if constexpr (VIN == 8) {
+      if constexpr (VIN == 16) {
+        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+        vst[r][0] = x[0]; vst[r][1] = x[1]; vst[r][2] = x[2]; vst[r][3] = x[3];
+      } else if constexpr (VIN == 8) {
         u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, 0);
         vst[r][0] = x[0]; vst[r][1] = x[1];
       } else if constexpr (VIN == 4) {
@@ -703,7 +720,7 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   // the grid (B*H query-tile rows) fits in int32.
   // One head's rows must stay addressable by 32-bit buffer offsets.
   if (N > (int64_t)1 << 22 || B * H > (int64_t)1 << 24) return FA_ERR_SHAPE;
-  const int64_t tiles = (N + kBR - 1) / kBR;
+  const int64_t tiles = (N + kMinBR - 1) / kMinBR;
   if (B * H * tiles > INT32_MAX) return FA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -713,11 +730,13 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
 }
 
 template <int DT, int D, bool CAUSAL>
-int launch_t(const Params& prm, hipStream_t stream) {
-  void* args[] = {const_cast<Params*>(&prm)};
+int launch_t(Params prm, hipStream_t stream) {
+  using S = Shape<DT, D>;
+  prm.n_qtiles = (prm.N + S::br - 1) / S::br;
+  void* args[] = {&prm};
   const dim3 grid((unsigned)(prm.bh * prm.n_qtiles));
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL>),
-                                 grid, dim3(kThreads), args, 0, stream);
+                                 grid, dim3(S::threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -740,7 +759,7 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   prm.o = static_cast<_Float16*>(o);
   prm.lse = lse;
   prm.N = (int)N;
-  prm.n_qtiles = (int)((N + kBR - 1) / kBR);
+  prm.n_qtiles = 0;  // set per kernel shape at launch
   prm.bh = (int)(B * H);
   prm.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
