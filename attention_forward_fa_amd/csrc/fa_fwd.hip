@@ -31,7 +31,7 @@
 //     P V operand is one ds_read_b128;
 //   * per-head buffer resources return zeros past row N, so ragged tails need
 //     no bounds branches (keys past N are masked to -inf in the scores);
-//   * software pipeline: iteration j issues the loads of K(j+2) and V(j+1)
+//   * software pipeline: iteration j issues the loads of K(j+3) and V(j+1)
 //     and, in one run of MFMAs, P V of block j-1 followed by QK^T of block
 //     j+1, with the softmax of block j and the V^T store of block j placed
 //     between the MFMAs; one workgroup barrier per block;
@@ -321,11 +321,14 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   constexpr int VIN = VD * ES;            // input bytes per key row per staging thread
   static_assert(kBC * D == 4 * VD * kThreads, "V staging must tile the workgroup");
 
-  // Two K stages and two V^T stages, each an array of its own: the compiler
-  // can then tell the buffers being filled from the ones being read and
-  // interleave the staging with the MFMA run.
+  // Four K stages (K is loaded three blocks ahead of its use) and two V^T
+  // stages, each an array of its own: the compiler can then tell the buffer
+  // an LDS load is filling from the ones being read, and neither waits for
+  // that load before the reads nor keeps the staging out of the MFMA run.
   __shared__ __attribute__((aligned(16))) uint8_t k_lds0[KBUF];
   __shared__ __attribute__((aligned(16))) uint8_t k_lds1[KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds2[KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds3[KBUF];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds0[VBUF];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds1[VBUF];
 
@@ -388,7 +391,8 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   // offset, which the buffer range check covers: rows at or past N read 0.
   // Blocks past the last one this workgroup needs are pointed beyond every
   // head's range, so they read 0 without touching memory.
-  constexpr int K_PER_W = (K_INSTR + kWaves - 1) / kWaves;
+  static_assert(K_INSTR % kWaves == 0, "K stage must split evenly over the waves");
+  constexpr int K_PER_W = K_INSTR / kWaves;
   int k_goff[K_PER_W];
 #pragma unroll
   for (int u = 0; u < K_PER_W; ++u) {
@@ -405,21 +409,21 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
     v_loff = vdgrp * VD * VTROW + keypos * 2;
   }
   constexpr int VW = (VIN + 3) / 4;  // dwords of one key row of a staging thread
-  uint32_t vst[4][VW];
+  typedef uint32_t VRegs[4][VW];     // one block's share of V, as loaded
+  VRegs vst;
   // Byte offset of key row kb, or one past every valid offset (N * KROWB is
   // at most 2^30) for a block the workgroup does not use.
-  auto block_off = [&](int kb) { return kb < kv_end ? kb * KROWB : (1 << 30); };
+  auto block_off = [&](int kb) __attribute__((always_inline)) { return kb < kv_end ? kb * KROWB : (1 << 30); };
 
-  auto load_k = [&](int kb, uint8_t* kbuf) {
+  auto load_k = [&](int kb, uint8_t* kbuf) __attribute__((always_inline)) {
     const int boff = block_off(kb);
 #pragma unroll
     for (int u = 0; u < K_PER_W; ++u) {
       const int inst = u * kWaves + wave;
-      if (K_INSTR % kWaves == 0 || inst < K_INSTR)
-        buffer_to_lds16(krs, kbuf + inst * kWave * 16, k_goff[u] + boff, 0);
+      buffer_to_lds16(krs, kbuf + inst * kWave * 16, k_goff[u] + boff, 0);
     }
   };
-  auto load_v = [&](int kb) {
+  auto load_v = [&](int kb, VRegs& vst) __attribute__((always_inline)) {
     const int boff = block_off(kb);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -439,7 +443,7 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   };
   // Convert the 4 x VD block held in registers to fp16 and write its VD rows
   // of V^T into the V^T buffer vbuf.
-  auto store_v = [&](uint8_t* vbuf) {
+  auto store_v = [&](const VRegs& vst, uint8_t* vbuf) __attribute__((always_inline)) {
     uint32_t h[4][VD / 2];  // fp16 pairs along d, per key
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -468,7 +472,7 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   // accesses complete, then s_barrier.  (__syncthreads would also wait for
   // every outstanding global load.)  Loads that must have landed before it
   // are waited for explicitly with vmcnt.
-  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto barrier = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   // ---- per-lane LDS operand addresses (block-independent parts) -------------
   // K (A operand of S^T): row kt*32 + lr, logical chunk(s) of k-step ks.
@@ -500,7 +504,7 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
 
   // S^T = K Q^T for the block in K buffer kbuf: two 32-key tiles.  The tiles
   // alternate so consecutive MFMAs are independent.
-  auto qk = [&](const uint8_t* kbuf, f32x16* st) {
+  auto qk = [&](const uint8_t* kbuf, f32x16* st) __attribute__((always_inline)) {
     st[0] = f32x16{};
     st[1] = f32x16{};
 #pragma unroll
@@ -521,10 +525,10 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   // Keys past N, and (causal) keys after the query, get score -inf.  A block
   // with every key masked for this lane leaves m_run, l_run unchanged and
   // contributes P = 0 (block 0 always holds a valid key for every row).
-  auto needs_mask = [&](int j) {
+  auto needs_mask = [&](int j) __attribute__((always_inline)) {
     return (j * kBC + kBC > N) || (CAUSAL && j * kBC + kBC - 1 > qw0);
   };
-  auto mask = [&](f32x16* st, int kb) {
+  auto mask = [&](f32x16* st, int kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -539,7 +543,7 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   // Online softmax of one block: new reference max (branch-free select),
   // P as fp16 pairs laid out as the B operand of O^T += V^T P^T, row-sum
   // update.  Returns the factor O^T must be scaled by when `rescale`.
-  auto softmax = [&](f32x16* st, PRegs& pw, bool& rescale) -> float {
+  auto softmax = [&](f32x16* st, PRegs& pw, bool& rescale) __attribute__((always_inline)) -> float {
     float m0 = st[0][0], m1 = st[1][0];  // two independent chains
 #pragma unroll
     for (int i = 1; i < 15; i += 2) {
@@ -587,7 +591,7 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   // the order the S^T accumulator holds and the order of V^T's permuted key
   // positions 16*s + 8*hh + i.  d tiles innermost: consecutive MFMAs update
   // different accumulators.
-  auto pv = [&](const uint8_t* vbuf, const PRegs& pw) {
+  auto pv = [&](const uint8_t* vbuf, const PRegs& pw) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -602,50 +606,58 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   };
 
   // ---- software pipeline ---------------------------------------------------------
-  // Iteration j fills K buffer j&1 with K(j+2) (that buffer held K(j), read
-  // in iteration j-1), writes V(j) -- loaded into registers during iteration
-  // j-1 -- to V^T buffer j&1 (last read in iteration j-1) and loads V(j+1)
-  // into those registers.  One run of MFMAs, P V of block j-1 (V^T buffer
+  // Iteration j writes V(j) -- loaded into registers during iteration j-1 --
+  // to V^T buffer j&1 (last read in iteration j-1), loads V(j+1) into the
+  // freed registers and K(j+3) into K stage (j+3)%4 (which held K(j-1), read
+  // in iteration j-2).  One run of MFMAs, P V of block j-1 (V^T buffer
   // (j-1)&1, P(j-1) kept from the previous iteration) followed by QK^T of
-  // block j+1 (K buffer (j+1)&1), carries the staging and the softmax of
-  // block j in the issue slots between the MFMAs.  Each wave then waits for
-  // its own loads and the workgroup meets at one barrier.  Loads are issued
-  // unconditionally (blocks past the end read 0), so the loop body is a
-  // straight line; the QK^T of the block after the last is computed and
-  // discarded, and iteration 0 multiplies a zero P(-1) with the zeroed
-  // V^T buffer 1.
+  // block j+1 (K stage (j+1)%4), carries the softmax of block j and the
+  // staging in the issue slots between the MFMAs.  Each wave then waits for
+  // its loads of the previous iteration (K(j+2) is read next iteration) --
+  // those of this iteration stay in flight; V(j+1) is waited for where it is
+  // stored -- and the workgroup meets at one barrier.  The loop is unrolled by four so every buffer is a
+  // compile-time choice.  Loads are issued unconditionally (blocks past the
+  // end read 0), so the loop body is a straight line and the outstanding-load
+  // counts are fixed; the QK^T of the block after the last is computed and
+  // discarded, and iteration 0 multiplies a zero P(-1) with the zeroed V^T
+  // buffer 1.
   for (int i = tid; i < VBUF / 16; i += kThreads) {
     reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0u, 0u, 0u, 0u};
   }
+  constexpr int NVM = K_PER_W + 4;  // global load instructions per wave per iteration
   load_k(0, k_lds0);
   load_k(kBC, k_lds1);
-  load_v(0);
-  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // this wave's K(0), K(1); V(0) may fly
+  load_v(0, vst);
+  load_k(2 * kBC, k_lds2);
+  // This wave's K(0) and K(1) have landed; V(0) and K(2) may still fly.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 + K_PER_W) : "memory");
   barrier();
 
   f32x16 sa[2], sb[2];
   PRegs pa, pb = {};
   qk(k_lds0, sa);
-  barrier();  // iteration 0 overwrites K buffer 0 with K(2)
+  barrier();
 
   constexpr int NPV = NDT * 4;     // P V MFMAs per block
   constexpr int NQK = 2 * NKS;     // QK^T MFMAs per block
   constexpr int VPM = (160 + NPV + NQK - 1) / (NPV + NQK);  // about 160 VALU per block
   constexpr int TPM = (kBC / 2 + NPV + NQK) / (NPV + NQK);  // kBC / 2 + 1 exponentials per block
-  constexpr int NVM = K_PER_W + 4;                          // global loads per wave
-  auto step = [&](int j, uint8_t* k_next, uint8_t* k_fill, const uint8_t* v_prev,
+  auto step = [&](int j, const uint8_t* k_next, uint8_t* k_fill, const uint8_t* v_prev,
                   uint8_t* v_fill, f32x16* s_cur, f32x16* s_next, PRegs& p_cur,
-                  const PRegs& p_prev) {
+                  const PRegs& p_prev) __attribute__((always_inline)) {
     if (needs_mask(j)) mask(s_cur, j * kBC);
-    load_k((j + 2) * kBC, k_fill);  // K(j+2)
-    store_v(v_fill);                // V(j) -> V^T
-    load_v((j + 1) * kBC);          // V(j+1) -> registers
-    pv(v_prev, p_prev);             // P V of block j-1
-    qk(k_next, s_next);             // QK^T of block j+1
+    store_v(vst, v_fill);             // V(j) -> V^T
+    load_v((j + 1) * kBC, vst);       // V(j+1) -> registers
+    // V(j+1) goes out before K(j+3): the wait for V(j+1) where it is stored
+    // then leaves K(j+3) in flight.
+    __builtin_amdgcn_sched_barrier(0);
+    load_k((j + 3) * kBC, k_fill);    // K(j+3)
+    pv(v_prev, p_prev);               // P V of block j-1
+    qk(k_next, s_next);               // QK^T of block j+1
     bool rescale;
     const float alpha = softmax(s_cur, p_cur, rescale);
-    mfma_run_pipeline<NPV, 1, NQK, KCH, 4, VPM, TPM, VD / 2, NVM>();
+    mfma_run_pipeline<NPV, 1, NQK, KCH, 4, VPM, TPM, 0, K_PER_W>();
     // Keep the softmax in this block, beside the MFMAs: its results are only
     // used next iteration, and the compiler would otherwise sink it there.
 #pragma unroll
@@ -659,24 +671,30 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
 #pragma unroll
       for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVM) : "memory");
     barrier();
   };
-  auto last_pv = [&](const uint8_t* vbuf, const PRegs& p_last) {
+  // Iteration j with j % 4 == 0, 1, 2, 3.
+  auto step0 = [&](int j) __attribute__((always_inline)) { step(j, k_lds1, k_lds3, v_lds1, v_lds0, sa, sb, pa, pb); };
+  auto step1 = [&](int j) __attribute__((always_inline)) { step(j, k_lds2, k_lds0, v_lds0, v_lds1, sb, sa, pb, pa); };
+  auto step2 = [&](int j) __attribute__((always_inline)) { step(j, k_lds3, k_lds1, v_lds1, v_lds0, sa, sb, pa, pb); };
+  auto step3 = [&](int j) __attribute__((always_inline)) { step(j, k_lds0, k_lds2, v_lds0, v_lds1, sb, sa, pb, pa); };
+  auto last_pv = [&](const uint8_t* vbuf, const PRegs& p_last) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS load outlives the loop
     pv(vbuf, p_last);
     mfma_read_pipeline<NPV, 1, (NPV < 8 ? NPV : 8)>();
   };
-  int j = 0;
-  for (; j + 1 < nblk; j += 2) {
-    step(j, k_lds1, k_lds0, v_lds1, v_lds0, sa, sb, pa, pb);
-    step(j + 1, k_lds0, k_lds1, v_lds0, v_lds1, sb, sa, pb, pa);
+  // The loop runs to the next multiple of four blocks: blocks past the last
+  // one are fully masked (keys past N, or causal keys after every query of the
+  // workgroup), so they change neither m, l nor O.  One copy of the loop body
+  // keeps the register allocation of the steady state.
+  for (int j = 0; j < nblk; j += 4) {
+    step0(j);
+    step1(j + 1);
+    step2(j + 2);
+    step3(j + 3);
   }
-  if (j < nblk) {
-    step(j, k_lds1, k_lds0, v_lds1, v_lds0, sa, sb, pa, pb);
-    last_pv(v_lds0, pa);  // block nblk-1 = j is even
-  } else {
-    last_pv(v_lds1, pb);  // block nblk-1 = j-1 is odd
-  }
+  last_pv(v_lds1, pb);  // the last iteration is odd: P in pb, V^T in buffer 1
 
   // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
