@@ -302,6 +302,23 @@ def pin_fwd_layout():
             _close(Lr[b, h], Lh[rows], 1e-13, 1e-13, "row subset LSE")
 
 
+def pin_lse_merge():
+    # Attention over a key set split into parts merges exactly from the
+    # parts' outputs: LSE = ln sum_g exp(LSE_g), O = sum_g exp(LSE_g - LSE) O_g.
+    # This is the exchange a sequence split over several GPUs would use, and
+    # it holds only if LSE is the natural-log sum of exp of the scaled scores.
+    n, m, d = 37, 53, 8
+    q = _rand((n, d), 1300)
+    k, v = _rand((m, d), 1301), _rand((m, d), 1302)
+    O, L = A.attention_head(q, k, v, 0.7, False)
+    cuts = [0, 11, 30, m]
+    parts = [A.attention_head(q, k[a:b], v[a:b], 0.7, False) for a, b in zip(cuts, cuts[1:])]
+    Lm = np.logaddexp.reduce(np.stack([p[1] for p in parts]), axis=0)
+    Om = sum(np.exp(p[1] - Lm)[:, None] * p[0] for p in parts)
+    _close(Lm, L, 1e-12, 1e-14, "merged LSE")
+    _close(Om, O, 1e-12, 0, "merged O")
+
+
 PINS = [
     pin_decimal_bruteforce,
     pin_decimal_large_scores,
@@ -317,4 +334,5 @@ PINS = [
     pin_joint_permutation,
     pin_score_overflow_stress,
     pin_fwd_layout,
+    pin_lse_merge,
 ]
