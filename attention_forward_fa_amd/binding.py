@@ -33,6 +33,8 @@ SIGNATURES = {
                               ctypes.c_int, ctypes.c_int, _P]),
     "fa_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                   ctypes.c_float, ctypes.c_int, _P]),
+    "fa_fwd_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                                 ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }
@@ -81,31 +83,37 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+LAYOUTS = {"bhnd": 0, "bnhd": 1}
+
+
 def _validate(q, k, v):
     if not (isinstance(q, torch.Tensor) and isinstance(k, torch.Tensor)
             and isinstance(v, torch.Tensor)):
         raise TypeError("q, k, v must be torch tensors")
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+        raise ValueError("q, k, v must share one 4-d shape")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _TORCH_DTYPE_CODE:
         raise TypeError("q, k, v must all be float16, bfloat16 or float8_e4m3fn")
     for t in (q, k, v):
         if not t.is_cuda:
             raise ValueError("q, k, v must be device tensors")
         if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous [B, H, N, d]")
+            raise ValueError("q, k, v must be contiguous")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
 
 
-def _outputs(q, out, lse):
-    B, H, N, d = q.shape
+def _outputs(q, out, lse, layout="bhnd"):
+    if layout == "bnhd":
+        B, N, H, d = q.shape
+    else:
+        B, H, N, d = q.shape
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float16, device=q.device)
+        out = torch.empty(q.shape, dtype=torch.float16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != (B, H, N, d) or out.dtype != torch.float16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float16 [B, H, N, d] tensor")
+    if out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 tensor shaped like q")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     return out, lse
@@ -157,6 +165,41 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, descale_q: torch.
         st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(descale_q), _ptr(descale_k),
                             _ptr(descale_v), _ptr(out), _ptr(lse), B, H, N, d, scale,
                             int(bool(causal)), stream)
+    _check(st)
+    return out, lse
+
+
+def fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bhnd",
+           causal: bool = False, scale: Optional[float] = None,
+           descales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+           out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fa_fwd_ex: q, k, v, out in [B, H, N, d] ("bhnd") or [B, N, H, d] ("bnhd");
+    lse is [B, H, N] either way.  descales (fp8 only): float32 [B*H] each."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    _validate(q, k, v)
+    if layout == "bnhd":
+        B, N, H, d = q.shape
+    else:
+        B, H, N, d = q.shape
+    dq = dk = dv = None
+    if descales is not None:
+        if q.dtype != torch.float8_e4m3fn:
+            raise TypeError("descales apply to float8_e4m3fn inputs only")
+        for t in descales:
+            if (t.dtype != torch.float32 or t.numel() != B * H or not t.is_contiguous()
+                    or t.device != q.device):
+                raise ValueError("descales must be contiguous float32 device tensors of B*H values")
+        dq, dk, dv = descales
+    out, lse = _outputs(q, out, lse, layout)
+    scale = _default_scale(d) if scale is None else float(scale)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(out),
+                           _ptr(lse), B, H, N, d, scale, int(bool(causal)),
+                           _TORCH_DTYPE_CODE[q.dtype], LAYOUTS[layout], stream)
     _check(st)
     return out, lse
 

@@ -232,13 +232,16 @@ struct Params {
   _Float16* o;
   float* lse;
   int N;
+  int H;
   int n_qtiles;
-  int bh;  // B*H
+  int bh;      // B*H
+  int layout;  // FA_LAYOUT_BHND or FA_LAYOUT_BNHD (q, k, v and o alike)
   float scale;
 };
 
-// Buffer resource over one head's [N, row_bytes] slice: loads past the end
-// return zeros, which is how ragged tails are read without bounds branches.
+// Buffer resource over one head's N rows (row r at byte r * row_stride, each
+// row_bytes long): loads past the last row return zeros, which is how ragged
+// tails are read without bounds branches.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, nbytes,
                                            0x00020000);
@@ -342,10 +345,24 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   int bh, qt;
   tile_of(blockIdx.x, p.bh, p.n_qtiles, CAUSAL, bh, qt);
   const int N = p.N;
-  const int64_t head_off = (int64_t)bh * N * D;
-  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + head_off * ES, N * KROWB);
-  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + head_off * ES, N * KROWB);
-  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v + head_off * ES, N * KROWB);
+  // Element offset of the head's first row and the stride between its rows:
+  // [B, H, N, d] (rows of one head adjacent) or [B, N, H, d] (rows of one head
+  // H*d elements apart).  Q, K, V and O share the layout.
+  int64_t head_off;
+  int row_elems;
+  if (p.layout == FA_LAYOUT_BNHD) {
+    const int b = bh / p.H, h = bh - b * p.H;
+    head_off = ((int64_t)b * N * p.H + h) * D;
+    row_elems = p.H * D;
+  } else {
+    head_off = (int64_t)bh * N * D;
+    row_elems = D;
+  }
+  const int GRS = row_elems * ES;             // bytes between rows in global memory
+  const int head_bytes = (N - 1) * GRS + KROWB;  // <= 2^30, checked on the host
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + head_off * ES, head_bytes);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + head_off * ES, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v + head_off * ES, head_bytes);
 
   const int q0 = qt * kBR;              // first query row of the workgroup
   const int qw0 = q0 + wave * kQW;      // first query row of this wave
@@ -367,7 +384,7 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
     const int byte = (ks * E::kstep + hh * (E::kstep / 2)) * ES;
 #pragma unroll
     for (int w = 0; w < E::opnd_dwords; w += 4) {
-      u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, my_q * KROWB + byte + 4 * w, 0, 0);
+      u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, my_q * GRS + byte + 4 * w, 0, 0);
       qreg[ks].w[w + 0] = x[0];
       qreg[ks].w[w + 1] = x[1];
       qreg[ks].w[w + 2] = x[2];
@@ -398,10 +415,10 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   for (int u = 0; u < K_PER_W; ++u) {
     const int slot = (u * kWaves + wave) * kWave + lane;
     const int row = slot / KCPR, phys = slot % KCPR;
-    k_goff[u] = row * KROWB + ((phys ^ swz<KROWB>(row)) * 16);
+    k_goff[u] = row * GRS + ((phys ^ swz<KROWB>(row)) * 16);
   }
   const int vquad = tid % 16, vdgrp = tid / 16;
-  const int v_goff = 4 * vquad * KROWB + vdgrp * VIN;
+  const int v_goff = 4 * vquad * GRS + vdgrp * VIN;
   int v_loff;
   {
     const int qq = vquad % 4;  // quad inside its 16-key group -> position quad
@@ -411,9 +428,9 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   constexpr int VW = (VIN + 3) / 4;  // dwords of one key row of a staging thread
   typedef uint32_t VRegs[4][VW];     // one block's share of V, as loaded
   VRegs vst;
-  // Byte offset of key row kb, or one past every valid offset (N * KROWB is
-  // at most 2^30) for a block the workgroup does not use.
-  auto block_off = [&](int kb) __attribute__((always_inline)) { return kb < kv_end ? kb * KROWB : (1 << 30); };
+  // Byte offset of key row kb, or one past every valid offset (a head spans
+  // at most 2^30 bytes) for a block the workgroup does not use.
+  auto block_off = [&](int kb) __attribute__((always_inline)) { return kb < kv_end ? kb * GRS : (1 << 30); };
 
   auto load_k = [&](int kb, uint8_t* kbuf) __attribute__((always_inline)) {
     const int boff = block_off(kb);
@@ -427,7 +444,7 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
     const int boff = block_off(kb);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int off = v_goff + r * KROWB + boff;
+      const int off = v_goff + r * GRS + boff;
       if constexpr (VIN == 16) {
         u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
         vst[r][0] = x[0]; vst[r][1] = x[1]; vst[r][2] = x[2]; vst[r][3] = x[3];
@@ -700,7 +717,7 @@ __global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Para
   const float l_tot = sum_pair32(l_run);
   if (my_q < N) {
     const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;
-    _Float16* orow = p.o + head_off + (int64_t)my_q * D;
+    _Float16* orow = p.o + head_off + (int64_t)my_q * row_elems;
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
@@ -722,8 +739,9 @@ bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>
 
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
-               bool* empty) {
+               int layout, bool* empty) {
   *empty = false;
+  if (layout != FA_LAYOUT_BHND && layout != FA_LAYOUT_BNHD) return FA_ERR_LAYOUT;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3)
@@ -738,6 +756,9 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   // the grid (B*H query-tile rows) fits in int32.
   // One head's rows must stay addressable by 32-bit buffer offsets.
   if (N > (int64_t)1 << 22 || B * H > (int64_t)1 << 24) return FA_ERR_SHAPE;
+  // [B, N, H, d]: one head's rows span N*H*d elements.
+  const int64_t esize = dtype == FA_DTYPE_FP8_E4M3 ? 1 : 2;
+  if (layout == FA_LAYOUT_BNHD && N * H * d * esize > (int64_t)1 << 30) return FA_ERR_SHAPE;
   const int64_t tiles = (N + kMinBR - 1) / kMinBR;
   if (B * H * tiles > INT32_MAX) return FA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
@@ -766,7 +787,7 @@ int launch_dt(const Params& prm, int d, int causal, hipStream_t stream) {
 
 int run(const void* q, const void* k, const void* v, const float* dq, const float* dk,
         const float* dv, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
-        float scale, int causal, int dtype, void* stream) {
+        float scale, int causal, int dtype, int layout, void* stream) {
   Params prm;
   prm.q = static_cast<const uint8_t*>(q);
   prm.k = static_cast<const uint8_t*>(k);
@@ -777,8 +798,10 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   prm.o = static_cast<_Float16*>(o);
   prm.lse = lse;
   prm.N = (int)N;
+  prm.H = (int)H;
   prm.n_qtiles = 0;  // set per kernel shape at launch
   prm.bh = (int)(B * H);
+  prm.layout = layout;
   prm.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
@@ -794,9 +817,10 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
                       int dtype, void* stream) {
   bool empty;
-  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, &empty);
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, FA_LAYOUT_BHND, &empty);
   if (st != FA_OK || empty) return st;
-  return run(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, d, scale, causal, dtype, stream);
+  return run(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, d, scale, causal, dtype,
+             FA_LAYOUT_BHND, stream);
 }
 
 extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* descale_q,
@@ -804,13 +828,34 @@ extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, const flo
                           int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
                           void* stream) {
   bool empty;
-  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, FA_DTYPE_FP8_E4M3, &empty);
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, FA_DTYPE_FP8_E4M3,
+                      FA_LAYOUT_BHND, &empty);
   if (st != FA_OK || empty) return st;
   if (!descale_q || !descale_k || !descale_v) return FA_ERR_NULL;
   if (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4))
     return FA_ERR_ALIGN;
   return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal,
-             FA_DTYPE_FP8_E4M3, stream);
+             FA_DTYPE_FP8_E4M3, FA_LAYOUT_BHND, stream);
+}
+
+extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, const float* descale_q,
+                         const float* descale_k, const float* descale_v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                         int dtype, int layout, void* stream) {
+  bool empty;
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, layout, &empty);
+  if (st != FA_OK || empty) return st;
+  if (dtype == FA_DTYPE_FP8_E4M3) {
+    const int given = (descale_q != nullptr) + (descale_k != nullptr) + (descale_v != nullptr);
+    if (given != 0 && given != 3) return FA_ERR_NULL;
+    if (given == 3 &&
+        (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
+      return FA_ERR_ALIGN;
+  } else {
+    descale_q = descale_k = descale_v = nullptr;  // not used by fp16 / bf16
+  }
+  return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal, dtype,
+             layout, stream);
 }
 
 extern "C" const char* fa_status_string(int status) {
@@ -824,6 +869,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
     case FA_ERR_SCALE: return "scale must be finite and positive";
     case FA_ERR_CAUSAL: return "causal must be 0 or 1";
+    case FA_ERR_LAYOUT: return "layout must be FA_LAYOUT_BHND or FA_LAYOUT_BNHD";
     default: return "unknown status";
   }
 }

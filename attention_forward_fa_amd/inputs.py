@@ -133,10 +133,24 @@ CONFIGS = (
 )
 
 
+# Further benchmark shapes from the pages (no new arithmetic, same recipe):
+# the four forward shapes of the seven-backend table of "TCA 51%，MFU 不足
+# 8%——GPU 的隐藏性能损耗" (S = 512, D = 64, B*H = 512; S = 1024 / 2048 / 4096,
+# D = 128, B*H = 64 / 16 / 8, non-causal; the B x H split is not printed, so one
+# is chosen), of which S = 1024, D = 128, B*H = 64 is also the workload the
+# B300 page's harness lines fit (fp16, non-causal).
+EXTRA_WORKLOADS = (
+    ("fp16_b16h32_n512_d64", 16, 32, 512, 64, "fp16", False, 6),
+    ("fp16_b4h16_n1024_d128", 4, 16, 1024, 128, "fp16", False, 7),
+    ("fp16_b1h16_n2048_d128", 1, 16, 2048, 128, "fp16", False, 8),
+    ("fp16_b1h8_n4096_d128", 1, 8, 4096, 128, "fp16", False, 9),
+)
+
+
 def config(name_or_index) -> tuple:
     if isinstance(name_or_index, int):
         return CONFIGS[name_or_index]
-    for c in CONFIGS:
+    for c in CONFIGS + EXTRA_WORKLOADS:
         if c[0] == name_or_index:
             return c
     raise KeyError(name_or_index)

@@ -37,7 +37,11 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="workload name (attention_forward_fa_amd.inputs.CONFIGS)")
+                    help="workload name (attention_forward_fa_amd.inputs.CONFIGS or "
+                         "EXTRA_WORKLOADS)")
+    ap.add_argument("--layout", default="bhnd", choices=["bhnd", "bnhd"],
+                    help="tensor layout of q, k, v, o: [B,H,N,d] (fa_fwd) or [B,N,H,d] "
+                         "(fa_fwd_ex)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -113,7 +117,7 @@ class ClockSampler:
         return sum(s) / len(s) if s else None
 
 
-def time_gpu(inp, steps, warmup, clock=None):
+def time_gpu(inp, steps, warmup, clock=None, layout="bhnd"):
     """Average seconds per fa_fwd call, HIP events on the launch stream; with a
     ClockSampler, afterwards the mean graphics clock under the same load."""
     import torch
@@ -121,11 +125,19 @@ def time_gpu(inp, steps, warmup, clock=None):
     from attention_forward_fa_amd import binding
 
     q, k, v, ds = binding.to_device(inp, "cuda")
-    out = torch.empty((inp.B, inp.H, inp.N, inp.d), dtype=torch.float16, device="cuda")
     lse = torch.empty((inp.B, inp.H, inp.N), dtype=torch.float32, device="cuda")
+    if layout == "bnhd":
+        def bnhd(t):
+            raw = t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16)
+            return raw.permute(0, 2, 1, 3).contiguous().view(t.dtype)
+        q, k, v = bnhd(q), bnhd(k), bnhd(v)
+    out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
 
     def step():
-        if inp.dtype == "fp8":
+        if layout == "bnhd":
+            binding.fwd_ex(q, k, v, layout="bnhd", causal=inp.causal, scale=inp.scale,
+                           descales=ds, out=out, lse=lse)
+        elif inp.dtype == "fp8":
             binding.fwd_fp8(q, k, v, *ds, causal=inp.causal, scale=inp.scale, out=out, lse=lse)
         else:
             binding.fwd(q, k, v, causal=inp.causal, scale=inp.scale, out=out, lse=lse)
@@ -176,11 +188,11 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_fwd_fp16_d128_n4096_traffic
 KERNEL_SOURCE = os.path.join(ROOT, "attention_forward_fa_amd", "csrc", "fa_fwd.hip")
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, layout="bhnd"):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE profile, or None
     when that profile is for another workload or an older kernel source."""
     import hashlib
-    if workload != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_PROFILE):
+    if workload != DEFAULT_WORKLOAD or layout != "bhnd" or not os.path.exists(TRAFFIC_PROFILE):
         return None
     vals, sha = {}, None
     for line in open(TRAFFIC_PROFILE, encoding="utf-8"):
@@ -225,14 +237,14 @@ def main(argv=None):
     name, B, H, N, d, dtype, causal, seed = inputs.config(args.workload)
     inp = inputs.draw(B, H, N, d, dtype, causal, seed)
     clock = ClockSampler()
-    sec = time_gpu(inp, args.steps, args.warmup, clock)
+    sec = time_gpu(inp, args.steps, args.warmup, clock, args.layout)
     flops, tf, peak = describe(inp, sec)
     if args.sweep:
-        for cfg in inputs.CONFIGS:
+        for cfg in inputs.CONFIGS + inputs.EXTRA_WORKLOADS:
             x = inputs.draw(*cfg[1:8])
-            s = time_gpu(x, max(10, args.steps // 4), args.warmup)
+            s = time_gpu(x, max(10, args.steps // 4), args.warmup, None, args.layout)
             _, t, pk = describe(x, s)
-            print(json.dumps({"workload": cfg[0], "ms": round(s * 1e3, 4),
+            print(json.dumps({"workload": cfg[0], "layout": args.layout, "ms": round(s * 1e3, 4),
                               "tflops": round(t, 2), "frac": round(t / pk, 4)}),
                   file=sys.stderr, flush=True)
     rec = {
@@ -248,12 +260,12 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": {"fp16": "f16", "bf16": "bf16", "fp8": "fp8e4m3"}[dtype],
         "data": "synthetic",
-        "config": {"workload": name, "B": B, "H": H, "N": N, "d": d,
+        "config": {"workload": name, "layout": args.layout, "B": B, "H": H, "N": N, "d": d,
                    "input_dtype": dtype, "causal": bool(causal), "seed": seed,
                    "outputs": "O fp16 + LSE fp32", "accumulate": "fp32"},
         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tf / peak, 4),
-                     "traffic": measured_traffic(name)},
+                     "traffic": measured_traffic(name, args.layout)},
         "frac_of_peak": round(tf / peak, 4),
         # The dense peak assumes the 2400 MHz top clock; under this load the
         # package power limit holds the clock lower.  Same work, measured clock:

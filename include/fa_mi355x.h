@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_DTYPE_FP16 = 0,      /* IEEE binary16 */
@@ -66,8 +66,15 @@ typedef enum {
   FA_ERR_ALIGN = -5,      /* a pointer is not aligned as required */
   FA_ERR_LAUNCH = -6,     /* the HIP runtime refused the kernel launch */
   FA_ERR_SCALE = -7,      /* scale not finite and positive */
-  FA_ERR_CAUSAL = -8      /* causal not 0 or 1 */
+  FA_ERR_CAUSAL = -8,     /* causal not 0 or 1 */
+  FA_ERR_LAYOUT = -9      /* unknown tensor layout */
 } fa_status;
+
+/* Memory layout of q, k, v and o (lse is always [B, H, N]). */
+typedef enum {
+  FA_LAYOUT_BHND = 0,     /* [B, H, N, d]: the rows of one head are adjacent */
+  FA_LAYOUT_BNHD = 1      /* [B, N, H, d]: row n of every head, then row n+1 */
+} fa_layout;
 
 /*
  * fa_fwd -- attention forward for fp16, bf16 or fp8 inputs.
@@ -95,6 +102,25 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v,
                const float* descale_v, void* o, float* lse,
                int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                int causal, void* stream);
+
+/*
+ * fa_fwd_ex -- the same operation for either tensor layout and any dtype.
+ * layout FA_LAYOUT_BHND gives exactly fa_fwd (or fa_fwd_fp8); with
+ * FA_LAYOUT_BNHD, q, k, v and o are [B, N, H, d] contiguous (element (b, n,
+ * h, i) at ((b*N + n)*H + h)*d + i), the layout the kernels of "Flash
+ * Attention CUDA Kernel 优化: 从 56 到 986 TFLOPS on B300" take (section
+ * V14, 坑二) -- while lse stays [B, H, N].  The
+ * descale arrays are read for fp8 only: all three NULL means unit scales,
+ * otherwise all three must be given (FA_ERR_NULL) as for fa_fwd_fp8.  For
+ * [B, N, H, d] one head's rows span N*H*d elements, which must stay within
+ * 2^30 bytes (FA_ERR_SHAPE).  An unknown layout returns FA_ERR_LAYOUT.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v,
+              const float* descale_q, const float* descale_k,
+              const float* descale_v, void* o, float* lse,
+              int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+              int causal, int dtype, int layout, void* stream);
 
 /* Short English description of a status code (never NULL, static storage). */
 const char* fa_status_string(int status);

@@ -122,3 +122,47 @@ def test_empty_problem_is_a_noop(kw):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(FileNotFoundError):
         binding.load_library(str(tmp_path / "missing.so"))
+
+
+def _call_ex(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, dq=None, dk=None, dv=None, o=O, lse=L, B=1, H=2, N=256, d=128,
+                scale=0.1, causal=0, dtype=0, layout=1, stream=None)
+    args.update(kw)
+    return lib.fa_fwd_ex(args["q"], args["k"], args["v"], args["dq"], args["dk"], args["dv"],
+                         args["o"], args["lse"], args["B"], args["H"], args["N"], args["d"],
+                         args["scale"], args["causal"], args["dtype"], args["layout"],
+                         args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=2), "FA_ERR_LAYOUT"),
+    (dict(layout=-1), "FA_ERR_LAYOUT"),
+    (dict(q=None), "FA_ERR_NULL"),
+    (dict(d=96), "FA_ERR_HEAD_DIM"),
+    (dict(dtype=5), "FA_ERR_DTYPE"),
+    (dict(o=O + 4), "FA_ERR_ALIGN"),
+    # fp8: descales all or none
+    (dict(dtype=2, dq=A + 0x5000), "FA_ERR_NULL"),
+    (dict(dtype=2, dq=A + 0x5000, dk=A + 0x6000), "FA_ERR_NULL"),
+    (dict(dtype=2, dq=A + 0x5002, dk=A + 0x6000, dv=A + 0x7000), "FA_ERR_ALIGN"),
+    # [B, N, H, d]: one head's rows span N*H*d elements, at most 2^30 bytes
+    (dict(N=1 << 20, H=1 << 9, d=128, dtype=1), "FA_ERR_SHAPE"),
+    (dict(N=1 << 20, H=1 << 4, d=128, dtype=2, layout=1), "FA_ERR_SHAPE"),
+])
+def test_fa_fwd_ex_rejects(kw, status):
+    assert _call_ex(**kw) == _header_constants()[status]
+
+
+def test_fa_fwd_ex_shape_limit_is_per_layout():
+    # The same N*H*d that [B, N, H, d] refuses passes the size checks for
+    # [B, H, N, d]; a NULL q (checked after the sizes) stops it before launch.
+    big = dict(N=1 << 20, H=1 << 4, d=128, dtype=2, q=None)
+    assert _call_ex(layout=1, **big) == _header_constants()["FA_ERR_SHAPE"]
+    assert _call_ex(layout=0, **big) == _header_constants()["FA_ERR_NULL"]
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_fa_fwd_ex_empty_is_a_noop(layout):
+    assert _call_ex(layout=layout, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert _call_ex(layout=layout, B=0) == 0
