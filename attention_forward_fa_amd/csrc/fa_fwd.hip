@@ -82,17 +82,22 @@ struct QKOperand {
   uint32_t w[Elem<DT>::opnd_dwords];
 };
 
-// Waves per workgroup, two per SIMD either way.  Eight (one workgroup per CU)
-// where a block carries 32 MFMAs per wave (fp16 / bf16 at d = 128); four (two
+// Waves per workgroup.  Eight (one workgroup per CU, two waves per SIMD) where
+// a block carries 32 MFMAs per wave (fp16 / bf16 at d = 128); four (two
 // workgroups per CU, which drift apart and fill each other's barrier waits)
-// where a block has fewer MFMAs per softmax instruction (d = 64, fp8).
+// where a block has fewer MFMAs per softmax instruction (d = 64, fp8).  The
+// eight-wave kernels have a four-wave twin (128-row tiles, one wave per SIMD)
+// for grids that would leave most CUs idle.
 template <int DT, int D>
+constexpr int default_waves() { return (D == 128 && DT != FA_DTYPE_FP8_E4M3) ? 8 : 4; }
+template <int WAVES>
 struct Shape {
-  static constexpr int waves = (D == 128 && DT != FA_DTYPE_FP8_E4M3) ? 8 : 4;
+  static constexpr int waves = WAVES;
   static constexpr int threads = kWave * waves;
   static constexpr int br = kQW * waves;  // query rows per workgroup
 };
 constexpr int kMinBR = kQW * 4;           // smallest query tile of any kernel
+constexpr int kCUs = 256;                 // compute units of an MI355X
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma_qk(const QKOperand<DT>& a, const QKOperand<DT>& b,
@@ -300,12 +305,12 @@ __device__ __forceinline__ void tile_of(int w, int n_heads, int n_tiles, bool ca
   bh = head_slot * stride + xcd;
 }
 
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__((Shape<DT, D>::threads), 2) void fa_fwd_kernel(Params p) {
+template <int DT, int D, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Params p) {
   using E = Elem<DT>;
-  constexpr int kWaves = Shape<DT, D>::waves;
-  constexpr int kThreads = Shape<DT, D>::threads;
-  constexpr int kBR = Shape<DT, D>::br;
+  constexpr int kWaves = Shape<WAVES>::waves;
+  constexpr int kThreads = Shape<WAVES>::threads;
+  constexpr int kBR = Shape<WAVES>::br;
   constexpr int ES = E::bytes;
   constexpr int KROWB = D * ES;           // bytes per K row, global and LDS
   constexpr int KCPR = KROWB / 16;        // 16-byte chunks per K row
@@ -768,15 +773,28 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   return FA_OK;
 }
 
-template <int DT, int D, bool CAUSAL>
-int launch_t(Params prm, hipStream_t stream) {
-  using S = Shape<DT, D>;
+template <int DT, int D, bool CAUSAL, int WAVES>
+int launch_w(Params prm, hipStream_t stream) {
+  using S = Shape<WAVES>;
   prm.n_qtiles = (prm.N + S::br - 1) / S::br;
   void* args[] = {&prm};
   const dim3 grid((unsigned)(prm.bh * prm.n_qtiles));
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL>),
-                                 grid, dim3(S::threads), args, 0, stream);
+  hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, WAVES>), grid,
+      dim3(S::threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int DT, int D, bool CAUSAL>
+int launch_t(const Params& prm, hipStream_t stream) {
+  constexpr int W = default_waves<DT, D>();
+  if constexpr (W == 8) {
+    // With 256-row tiles filling at most half the CUs, 128-row tiles on all of
+    // them finish sooner although one wave per SIMD runs slower than two.
+    const int64_t wgs = (int64_t)prm.bh * ((prm.N + Shape<8>::br - 1) / Shape<8>::br);
+    if (2 * wgs <= kCUs) return launch_w<DT, D, CAUSAL, 4>(prm, stream);
+  }
+  return launch_w<DT, D, CAUSAL, W>(prm, stream);
 }
 
 template <int DT>
