@@ -113,6 +113,17 @@ def test_large_config_sampled(cfg):
     assert np.isfinite(o).all() and np.isfinite(l).all()
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_eight_wave_kernel_ragged(dtype, causal):
+    # B*H*ceil(N/256) = 165 workgroups: the 8-wave d=128 kernel (smaller grids
+    # take its 4-wave twin), with a ragged last tile and last key block.
+    inp = inputs.draw(1, 33, 1100, 128, dtype, causal, seed=31)
+    o, l = to_np(*gpu_run(inp), inp)
+    rows = _sample_rows(inp.N, seed=31)
+    check(inp, o, l, heads=[0, 1, 16, 32], rows=rows)
+
+
 # --- edge cases and closed forms -----------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
