@@ -58,6 +58,7 @@ class AttnInputs:
     descale_k: Optional[np.ndarray] = None
     descale_v: Optional[np.ndarray] = None
     seed: Optional[int] = None
+    do: Optional[np.ndarray] = None  # dL/dO bits (backward inputs), same storage type
 
     @property
     def shape(self):
@@ -119,6 +120,21 @@ def draw(B: int, H: int, N: int, d: int, dtype: str, causal: bool, seed: int,
     k = torch.randn(shape, generator=g, dtype=torch.float32)
     v = torch.randn(shape, generator=g, dtype=torch.float32)
     return from_float(q, k, v, dtype, causal, scale, seed)
+
+
+def draw_bwd(B: int, H: int, N: int, d: int, dtype: str, causal: bool, seed: int,
+             scale: Optional[float] = None) -> AttnInputs:
+    """Backward inputs: the forward workload of ``draw`` (same Q, K, V) plus
+    dO = dL/dO, iid N(0, 1) drawn next from the same generator, rounded to the
+    same storage type (fp16 / bf16)."""
+    if dtype not in ("fp16", "bf16"):
+        raise ValueError("the backward pass takes fp16 or bf16 inputs")
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    shape = (B, H, N, d)
+    q, k, v, do = (torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(4))
+    inp = from_float(q, k, v, dtype, causal, scale, seed)
+    inp.do = _bits(do.to(_TORCH_STORAGE[dtype]), dtype)
+    return inp
 
 
 # The five workloads: (name, B, H, N, d, dtype, causal, seed).  The first is the

@@ -37,9 +37,16 @@ Readings where the pages are silent:
   * rows are independent: a chunk of query rows is processed at a time only
     to bound memory, each row still sees all of its keys in one reduction.
 
+* Backward pass (gradients of a loss L given dO = dL/dO): the pages only
+  name it (the Zhihu article counts it as recomputation at about 4x the
+  forward FLOPs); the oracle takes the chain rule through O = P V,
+  P = softmax(S), S = scale * Q K^T written out: dV = P^T dO, dP = dO V^T,
+  dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik), dQ = scale dS K, dK = scale dS^T Q.
+
 Pinned by tests/test_oracle_pins.py (40-digit decimal brute force, the
-page's streaming recurrence, closed forms, invariants) and
-tests/test_oracle_codecs.py (storage-format decoders).
+page's streaming recurrence, closed forms, invariants; central finite
+differences and invariants of the gradients) and tests/test_oracle_codecs.py
+(storage-format decoders).
 """
 from __future__ import annotations
 
@@ -172,6 +179,37 @@ def attention_fwd(q, k, v, scale, causal, rows=None):
     return o, lse
 
 
+# ---------------------------------------------------------------------------
+# Attention backward, from the chain rule.
+# ---------------------------------------------------------------------------
+
+
+def _softmax_grad(p, dp):
+    """dS = P * (dP - rowsum(P * dP)): the softmax Jacobian applied row by row."""
+    return p * (dp - np.sum(p * dp, axis=1)[:, None])
+
+
+def attention_bwd_head(q, k, v, do, scale, causal, chunk=256):
+    """dQ, dK, dV [N, d] float64 of one head, for dO = dL/dO [N, d].
+
+    Chunks of query rows are processed at a time only to bound memory; dK and
+    dV sum the contributions of every chunk.
+    """
+    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+    n = q.shape[0]
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for a in range(0, n, chunk):
+        r = np.arange(a, min(a + chunk, n))
+        p, _ = _softmax_rows(_scores(q[r], k, scale, causal, r))
+        dv += p.T @ do[r]
+        ds = _softmax_grad(p, do[r] @ v.T)
+        dq[r] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r])
+    return dq, dk, dv
+
+
 def head_values(inp, b, h):
     """Exact float64 (q, k, v), each [N, d], of head (b, h) of an input set."""
     if inp.dtype == "fp16":
@@ -205,3 +243,21 @@ def run(inp, rows=None, heads=None):
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+def run_bwd(inp, heads=None):
+    """Oracle gradients for an input set with dO (inp.do): (dQ, dK, dV) float64,
+    each [len(heads), N, d] (heads: flat indices b*H + h, default all)."""
+    if inp.dtype not in ("fp16", "bf16"):
+        raise ValueError("the backward pass takes fp16 or bf16 inputs")
+    dec = decode_fp16 if inp.dtype == "fp16" else decode_bf16
+    if heads is None:
+        heads = range(inp.B * inp.H)
+    out = ([], [], [])
+    for f in heads:
+        b, h = divmod(int(f), inp.H)
+        q, k, v = head_values(inp, b, h)
+        g = attention_bwd_head(q, k, v, dec(inp.do[b, h]), float(inp.scale), bool(inp.causal))
+        for lst, x in zip(out, g):
+            lst.append(x)
+    return tuple(np.stack(x) for x in out)

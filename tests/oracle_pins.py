@@ -319,6 +319,65 @@ def pin_lse_merge():
     _close(Om, O, 1e-12, 0, "merged O")
 
 
+def _loss(q, k, v, do, scale, causal):
+    O, _ = A.attention_head(q, k, v, scale, causal)
+    return float(np.sum(do * O))
+
+
+def pin_bwd_finite_differences():
+    # Gradients of L = sum(dO * O) against central differences of the
+    # (separately pinned) forward: h = 1e-5 in float64 leaves ~1e-9 of
+    # truncation and rounding error.
+    n, d, h = 6, 3, 1e-5
+    q, k, v, do = (_rand((n, d), 1400 + t) for t in range(4))
+    for causal in (False, True):
+        dq, dk, dv = A.attention_bwd_head(q, k, v, do, 0.8, causal)
+        for name, x, g in (("dQ", q, dq), ("dK", k, dk), ("dV", v, dv)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = {"q": q, "k": k, "v": v}
+                args_m = dict(args_p)
+                key = name[1].lower()
+                args_p[key], args_m[key] = xp, xm
+                fd[idx] = (_loss(args_p["q"], args_p["k"], args_p["v"], do, 0.8, causal)
+                           - _loss(args_m["q"], args_m["k"], args_m["v"], do, 0.8, causal)) / (2 * h)
+            _close(g, fd, 1e-7, 0, f"{name} vs finite differences (causal={causal})")
+
+
+def pin_bwd_invariants():
+    # Shifting every key by u leaves each row's softmax unchanged, so
+    # sum_j dK_j = 0; rows of P sum to 1, so sum_j dV_j = sum_i dO_i; scaling
+    # Q by t is scaling S by t, as is scaling K, so sum dQ*Q = sum dK*K.
+    n, d = 40, 8
+    q, k, v, do = (_rand((n, d), 1500 + t) for t in range(4))
+    for causal in (False, True):
+        dq, dk, dv = A.attention_bwd_head(q, k, v, do, 0.6, causal)
+        _close(dk.sum(axis=0), np.zeros(d), 1e-12, 0, "sum of dK")
+        _close(dv.sum(axis=0), do.sum(axis=0), 1e-12, 0, "sum of dV")
+        _close(np.sum(dq * q), np.sum(dk * k), 1e-11, 0, "dQ.Q = dK.K")
+
+
+def pin_bwd_closed_forms():
+    n, d = 30, 4
+    q, k, v, do = (_rand((n, d), 1600 + t) for t in range(4))
+    # Constant V: O does not depend on the scores, so dQ = dK = 0.
+    vc = np.full((n, d), 0.75)
+    for causal in (False, True):
+        dq, dk, dv = A.attention_bwd_head(q, k, vc, do, 0.5, causal)
+        _close(dq, np.zeros_like(dq), 1e-13, 0, "constant V: dQ")
+        _close(dk, np.zeros_like(dk), 1e-13, 0, "constant V: dK")
+    # Causal: row 0 sees key 0 alone (its softmax is constant: dQ_0 = 0), and
+    # the last key is seen by the last row alone: dV_{N-1} = P_{N-1,N-1} dO_{N-1}.
+    dq, dk, dv = A.attention_bwd_head(q, k, v, do, 0.5, True)
+    _close(dq[0], np.zeros(d), 1e-14, 0, "causal row 0: dQ")
+    s = 0.5 * (k[: n] @ q[n - 1])
+    p_last = np.exp(s[n - 1] - s.max()) / np.sum(np.exp(s - s.max()))
+    _close(dv[n - 1], p_last * do[n - 1], 1e-13, 0, "causal last key: dV")
+
+
 PINS = [
     pin_decimal_bruteforce,
     pin_decimal_large_scores,
@@ -335,4 +394,7 @@ PINS = [
     pin_score_overflow_stress,
     pin_fwd_layout,
     pin_lse_merge,
+    pin_bwd_finite_differences,
+    pin_bwd_invariants,
+    pin_bwd_closed_forms,
 ]

@@ -85,6 +85,27 @@ def _head_qk_swapped(q, k, v, scale, causal, rows=None, chunk=256):
     return _orig_head(k, q, v, scale, causal, rows, chunk)
 
 
+_orig_bwd = A.attention_bwd_head
+
+
+def _softmax_grad_no_rowsum(p, dp):
+    return p * dp
+
+
+def _softmax_grad_sign(p, dp):
+    return p * (np.sum(p * dp, axis=1)[:, None] - dp)
+
+
+def _bwd_dk_unscaled(q, k, v, do, scale, causal, chunk=256):
+    dq, dk, dv = _orig_bwd(q, k, v, do, scale, causal, chunk)
+    return dq, dk / scale, dv
+
+
+def _bwd_dq_dk_swapped(q, k, v, do, scale, causal, chunk=256):
+    dq, dk, dv = _orig_bwd(q, k, v, do, scale, causal, chunk)
+    return dk, dq, dv
+
+
 MUTANTS = [
     ("_scores", _scores_no_scale),
     ("_scores", _scores_sqrt_scale),
@@ -97,6 +118,10 @@ MUTANTS = [
     ("_softmax_rows", _softmax_lse_log2),
     ("attention_head", _head_value_rows_reversed),
     ("attention_head", _head_qk_swapped),
+    ("_softmax_grad", _softmax_grad_no_rowsum),
+    ("_softmax_grad", _softmax_grad_sign),
+    ("attention_bwd_head", _bwd_dk_unscaled),
+    ("attention_bwd_head", _bwd_dq_dk_swapped),
 ]
 
 
