@@ -35,6 +35,8 @@ SIGNATURES = {
                                   ctypes.c_float, ctypes.c_int, _P]),
     "fa_fwd_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                  ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]),
+    "fa_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                              ctypes.c_float, ctypes.c_int, ctypes.c_int, _P]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }
@@ -202,6 +204,37 @@ def fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bhn
                            _TORCH_DTYPE_CODE[q.dtype], LAYOUTS[layout], stream)
     _check(st)
     return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, causal: bool = False, scale: Optional[float] = None):
+    """dQ, dK, dV (fp32 [B, H, N, d]) and delta = rowsum(dO * O) (fp32 [B, H, N])
+    for fp16 / bf16 q, k, v, dout, the forward's o (fp16) and lse."""
+    _validate(q, k, v)
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("the backward pass takes float16 or bfloat16 q, k, v")
+    B, H, N, d = q.shape
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must be contiguous, shaped and typed like q")
+    if o.shape != q.shape or o.dtype != torch.float16 or not o.is_contiguous():
+        raise ValueError("o must be the forward's contiguous float16 output")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous float32 [B, H, N] output")
+    for t in (dout, o, lse):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+                  for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    scale = _default_scale(d) if scale is None else float(scale)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(delta), B, H, N, d, scale, int(bool(causal)),
+                        _TORCH_DTYPE_CODE[q.dtype], stream)
+    _check(st)
+    return dq, dk, dv, delta
 
 
 # Storage dtype names of the input generator -> torch dtypes.

@@ -10,7 +10,7 @@ import tempfile
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "libfa_mi355x.so")
-SOURCES = [os.path.join(PKG_DIR, "csrc", "fa_fwd.hip")]
+SOURCES = [os.path.join(PKG_DIR, "csrc", "fa_fwd.hip"), os.path.join(PKG_DIR, "csrc", "fa_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
 

@@ -1,0 +1,562 @@
+// Fused attention backward for MI355X (gfx950, CDNA4): the gradients dQ, dK,
+// dV of a loss L, given dO = dL/dO, the inputs Q, K, V, and the forward's O
+// and LSE.  The probabilities are recomputed block by block from the saved
+// LSE (P_ij = exp(scale q_i.k_j - LSE_i)), so the N x N matrices never reach
+// device memory -- the recomputation the "TCA 51%，MFU 不足 8%" page counts
+// for the backward pass.  Chain rule through O = P V, P = softmax(S):
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Two kernels, run in this order on the caller's stream:
+//   * fa_bwd_dq: one workgroup per (b, h, 128-query tile), a wave per 32
+//     queries, shaped like the forward: S^T = K Q^T and dP^T = V dO^T with Q
+//     and dO held in registers as B operands, dS^T in registers, then
+//     dQ^T += K^T dS^T with K^T read transposed (ds_read_b64_tr_b16) from the
+//     row-major K block in LDS.  It also computes D_i for its queries from O
+//     and dO and stores it (delta), for the second kernel.
+//   * fa_bwd_dkdv: one workgroup per (b, h, 128-key tile), a wave per 32
+//     keys held in registers (K and V rows as B operands): S = Q K^T and
+//     dP = dO V^T per 64-query block, then dV^T += dO^T P and
+//     dK^T += Q^T dS with dO^T and Q^T read transposed from the row-major
+//     dO and Q blocks.
+// Blocks stream global -> LDS (buffer_load ... lds, XOR-swizzled 16-byte
+// chunks) into two buffers, one barrier per block; the loops are unrolled by
+// two so each buffer is its own LDS array.  Rows past N read as zeros and are
+// masked, as are causal pairs (key j > query i); a loop runs to an even block
+// count, the extra block fully masked.  P and dS enter the second products
+// in the input type (fp16 or bf16, round to nearest even); all accumulation
+// is fp32 and the gradients are stored as fp32.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_common.h"
+#include "fa_mi355x.h"
+
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = kWave * kBwdWaves;
+constexpr int kRW = 32;                 // rows owned by one wave
+constexpr int kBT = kRW * kBwdWaves;    // rows owned by one workgroup
+constexpr int kBS = 64;                 // rows of one streamed block
+
+struct BwdParams {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const _Float16* o;
+  const float* lse;
+  const uint8_t* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;
+  int N;
+  int n_tiles;
+  int bh;
+  float scale;
+};
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == FA_DTYPE_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return mfma_pv(a, b, c);
+  }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats as a pair of the input type, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == FA_DTYPE_BF16) {
+    bf16x2 h = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    return pack_f16x2(lo, hi);
+  }
+}
+
+// Element e (0 or 1) of a pair of the input type, as float (exact).
+template <int DT>
+__device__ __forceinline__ float elem(uint32_t w, int e) {
+  const uint32_t bits = e ? (w >> 16) : (w & 0xffffu);
+  if constexpr (DT == FA_DTYPE_BF16) {
+    return __uint_as_float(bits << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+  }
+}
+
+typedef __attribute__((address_space(3))) short4_t lds_short4_t_bwd;
+
+// Per-lane addresses into a row-major LDS block of ROWB-byte rows whose
+// 16-byte chunks carry the swizzle swz<ROWB>(row):
+//  * row operand (A of a 32x32x16 MFMA with rows as M): row r0 + lr, the 8
+//    d-values of k-step ks starting at ks*16 + 8*hh;
+//  * transposed operand (A with d as M and rows as the contraction): lane
+//    (grp, e, r) of each 16-lane group reads 4 d-values of one row; the
+//    transposing read hands each lane the 4 rows at its d-value.  Slot j of
+//    lane half hh in k-step s is row 16 s + 8 (j / 4) + 4 hh + (j % 4) --
+//    the order a 32x32 accumulator holds its rows, so the other operand can
+//    come straight from an accumulator.
+template <int ROWB>
+struct BlockAddr {
+  static constexpr int D = ROWB / 2;
+  static constexpr int NKS = D / 16;
+  static constexpr int NDT = D / 32;
+  int row[NKS];        // + tile_row * ROWB
+  int tr[NDT][2];      // + (16-row group) * ROWB
+  __device__ __forceinline__ void init(int lane) {
+    const int lr = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int chunk = (ks * 16 + 8 * hh) / 8;
+      row[ks] = lr * ROWB + ((chunk ^ swz<ROWB>(lr)) * 16);
+    }
+    const int grp = lane >> 4, li = lane & 15, e = li >> 2, r = li & 3;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int rr = 8 * half + 4 * (grp >> 1) + e;
+        const int d = t * 32 + 16 * (grp & 1) + 4 * r;
+        tr[t][half] = rr * ROWB + (((d / 8) ^ swz<ROWB>(rr)) * 16) + (d % 8) * 2;
+      }
+  }
+};
+
+// A operand (32 rows x 16 d-values at k-step ks) of rows tile_row*32 .. +31.
+template <int ROWB>
+__device__ __forceinline__ u32x4 row_operand(const uint8_t* blk, const BlockAddr<ROWB>& a,
+                                             int tile, int ks) {
+  return *reinterpret_cast<const u32x4*>(blk + tile * 32 * ROWB + a.row[ks]);
+}
+
+// A operand (32 d-values of d tile t x 16 rows 16*g .. +15, in accumulator
+// row order) read transposed from the row-major block.
+template <int ROWB>
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* blk, const BlockAddr<ROWB>& a, int t,
+                                            int g) {
+  const uint8_t* base = blk + g * 16 * ROWB;
+  short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t_bwd*)(base + a.tr[t][0]));
+  short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t_bwd*)(base + a.tr[t][1]));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// Streams 64-row blocks of one head's [N, D] tensor into LDS: block rows
+// land at row * ROWB with swizzled chunks; one 64-lane load instruction fills
+// 1 KB, the workgroup's waves share the instructions.  Rows at or past N,
+// and blocks past `end_row`, read zeros (the latter without memory traffic).
+template <int ROWB>
+struct BlockLoader {
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int INSTR = kBS * CPR / kWave;
+  static_assert(INSTR % kBwdWaves == 0, "block must split evenly over the waves");
+  static constexpr int PER_W = INSTR / kBwdWaves;
+  int goff[PER_W];
+  int wave;
+  __device__ __forceinline__ void init(int w, int lane) {
+    wave = w;
+#pragma unroll
+    for (int u = 0; u < PER_W; ++u) {
+      const int slot = (u * kBwdWaves + w) * kWave + lane;
+      const int row = slot / CPR, phys = slot % CPR;
+      goff[u] = row * ROWB + ((phys ^ swz<ROWB>(row)) * 16);
+    }
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint8_t* blk, int row0,
+                                       int end_row) const {
+    const int boff = row0 < end_row ? row0 * ROWB : (1 << 30);
+#pragma unroll
+    for (int u = 0; u < PER_W; ++u)
+      buffer_to_lds16(rs, blk + (u * kBwdWaves + wave) * kWave * 16, goff[u] + boff, 0);
+  }
+};
+
+// 4 bytes per lane from a buffer straight into LDS: lane t writes
+// lds_dst + 4 t; each lane's dword is range-checked on its own.
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rs, void* lds_dst,
+                                               int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_dst, 4, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ void bwd_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D = rowsum(dO * O)).
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr int ROWB = D * 2;
+  constexpr int NKS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int BLK = kBS * ROWB;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[BLK];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds1[BLK];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds0[BLK];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds1[BLK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lr = lane & 31, hh = lane >> 5;
+
+  int bh, qt;
+  tile_of(blockIdx.x, p.bh, p.n_tiles, CAUSAL, bh, qt);
+  const int N = p.N;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const int head_bytes = N * ROWB;
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t ors = head_rsrc(
+      reinterpret_cast<const uint8_t*>(p.o + head_off), head_bytes);
+  const __amdgpu_buffer_rsrc_t dors = head_rsrc(p.dout + head_off * 2, head_bytes);
+
+  const int q0 = qt * kBT;
+  const int my_q = q0 + wave * kRW + lr;
+  const float cs = p.scale * kLog2e;
+
+  // Q and dO rows of this lane's query (B operands), and D = dO . O.
+  u32x4 qreg[NKS], doreg[NKS];
+  float dpart = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int byte = my_q * ROWB + (ks * 16 + 8 * hh) * 2;
+    qreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(qrs, byte, 0, 0);
+    doreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(dors, byte, 0, 0);
+    const u32x4 ow = __builtin_amdgcn_raw_buffer_load_b128(ors, byte, 0, 0);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        dpart = fmaf(elem<DT>(doreg[ks][w], e), elem<FA_DTYPE_FP16>(ow[w], e), dpart);
+  }
+  const float dsum = sum_pair32(dpart);
+  const float lse_l2 = (my_q < N ? p.lse[(int64_t)bh * N + my_q] : 0.0f) * kLog2e;
+  if (hh == 0 && my_q < N) p.delta[(int64_t)bh * N + my_q] = dsum;
+
+  BlockAddr<ROWB> ka;
+  ka.init(lane);
+  BlockLoader<ROWB> ld;
+  ld.init(wave, lane);
+
+  int kv_end = N;
+  if constexpr (CAUSAL) kv_end = min(N, q0 + kBT);
+  const int nblk = (kv_end + kBS - 1) / kBS;
+
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
+
+  ld.load(krs, k_lds0, 0, kv_end);
+  ld.load(vrs, v_lds0, 0, kv_end);
+  bwd_barrier();
+
+  auto step = [&](int j, const uint8_t* kb, const uint8_t* vb, uint8_t* kn,
+                  uint8_t* vn) __attribute__((always_inline)) {
+    ld.load(krs, kn, (j + 1) * kBS, kv_end);  // next block, in flight during this one
+    ld.load(vrs, vn, (j + 1) * kBS, kv_end);
+    f32x16 st[2], dpt[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      st[t2] = f32x16{};
+      dpt[t2] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        st[t2] = mfma16<DT>(row_operand<ROWB>(kb, ka, t2, ks), qreg[ks], st[t2]);
+        dpt[t2] = mfma16<DT>(row_operand<ROWB>(vb, ka, t2, ks), doreg[ks], dpt[t2]);
+      }
+    mfma_read_pipeline<4 * NKS, 1, 4>();
+    // dS^T = P^T (dP^T - D), P^T = exp2(cs s - lse log2 e); masked pairs give 0.
+    uint32_t dsw[2][2][4];
+    const int kb0 = j * kBS;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        float ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int key = kb0 + t2 * 32 + 8 * ((i + e) / 4) + 4 * hh + ((i + e) % 4);
+          bool keep = key < N;
+          if constexpr (CAUSAL) keep = keep && key <= my_q;
+          const float pv = keep ? __builtin_amdgcn_exp2f(fmaf(st[t2][i + e], cs, -lse_l2)) : 0.0f;
+          ds[e] = pv * (dpt[t2][i + e] - dsum);
+        }
+        dsw[t2][i / 8][(i % 8) / 2] = pack2<DT>(ds[0], ds[1]);
+      }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+          const u32x4 b = {dsw[t2][s][0], dsw[t2][s][1], dsw[t2][s][2], dsw[t2][s][3]};
+          acc[t] = mfma16<DT>(tr_operand<ROWB>(kb, ka, t, 2 * t2 + s), b, acc[t]);
+        }
+    mfma_read_pipeline<4 * NDT, 2, 4>();
+    bwd_barrier();
+  };
+  for (int j = 0; j < nblk; j += 2) {
+    step(j, k_lds0, v_lds0, k_lds1, v_lds1);
+    step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+  }
+
+  if (my_q < N) {
+    float* row = p.dq + head_off + (int64_t)my_q * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = t * 32 + 8 * g + 4 * hh;
+        *reinterpret_cast<float4*>(row + d0) =
+            float4{acc[t][4 * g] * p.scale, acc[t][4 * g + 1] * p.scale,
+                   acc[t][4 * g + 2] * p.scale, acc[t][4 * g + 3] * p.scale};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV.
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int ROWB = D * 2;
+  constexpr int NKS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int BLK = kBS * ROWB;
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds0[BLK];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds1[BLK];
+  __shared__ __attribute__((aligned(16))) uint8_t do_lds0[BLK];
+  __shared__ __attribute__((aligned(16))) uint8_t do_lds1[BLK];
+  // LSE and D of the block's 64 queries.
+  __shared__ __attribute__((aligned(16))) float lse_lds0[kBS];
+  __shared__ __attribute__((aligned(16))) float lse_lds1[kBS];
+  __shared__ __attribute__((aligned(16))) float d_lds0[kBS];
+  __shared__ __attribute__((aligned(16))) float d_lds1[kBS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lr = lane & 31, hh = lane >> 5;
+
+  // Causal work shrinks with the key tile: tile_of hands out its heavy-first
+  // order in reverse tile index, so turn it around.
+  int bh, tt;
+  tile_of(blockIdx.x, p.bh, p.n_tiles, CAUSAL, bh, tt);
+  const int kt = CAUSAL ? p.n_tiles - 1 - tt : tt;
+  const int N = p.N;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const int head_bytes = N * ROWB;
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t dors = head_rsrc(p.dout + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = head_rsrc(
+      reinterpret_cast<const uint8_t*>(p.lse + (int64_t)bh * N), N * 4);
+  const __amdgpu_buffer_rsrc_t drs = head_rsrc(
+      reinterpret_cast<const uint8_t*>(p.delta + (int64_t)bh * N), N * 4);
+
+  const int k0 = kt * kBT;
+  const int my_k = k0 + wave * kRW + lr;
+  const float cs = p.scale * kLog2e;
+
+  // K and V rows of this lane's key (B operands of S = Q K^T, dP = dO V^T).
+  u32x4 kreg[NKS], vreg[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int byte = my_k * ROWB + (ks * 16 + 8 * hh) * 2;
+    kreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(krs, byte, 0, 0);
+    vreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(vrs, byte, 0, 0);
+  }
+
+  BlockAddr<ROWB> qa;
+  qa.init(lane);
+  BlockLoader<ROWB> ld;
+  ld.init(wave, lane);
+
+  // Query blocks that can see a key of this tile: all, or (causal) from the
+  // block holding query k0 on.
+  const int qb_begin = CAUSAL ? (k0 / kBS) : 0;
+  const int nblk = (N - qb_begin * kBS + kBS - 1) / kBS;
+
+  f32x16 acck[NDT], accv[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    acck[t] = f32x16{};
+    accv[t] = f32x16{};
+  }
+
+  // LSE and D rows of a block: wave 0 and wave 1, one dword per lane.
+  auto load_ld = [&](float* lse_dst, float* d_dst, int row0) __attribute__((always_inline)) {
+    const int off = (row0 < N ? row0 : N) * 4 + lane * 4;  // past N: zeros
+    if (wave == 0) buffer_to_lds4(lrs, lse_dst, off);
+    if (wave == 1) buffer_to_lds4(drs, d_dst, off);
+  };
+
+  ld.load(qrs, q_lds0, qb_begin * kBS, N);
+  ld.load(dors, do_lds0, qb_begin * kBS, N);
+  load_ld(lse_lds0, d_lds0, qb_begin * kBS);
+  bwd_barrier();
+
+  auto step = [&](int j, const uint8_t* qb, const uint8_t* db, const float* lb, const float* dlb,
+                  uint8_t* qn, uint8_t* dn, float* ln, float* dln) __attribute__((always_inline)) {
+    const int qrow0 = (qb_begin + j) * kBS;  // first query of this block
+    ld.load(qrs, qn, qrow0 + kBS, N);
+    ld.load(dors, dn, qrow0 + kBS, N);
+    load_ld(ln, dln, qrow0 + kBS);
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      s[t2] = f32x16{};
+      dp[t2] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        s[t2] = mfma16<DT>(row_operand<ROWB>(qb, qa, t2, ks), kreg[ks], s[t2]);
+        dp[t2] = mfma16<DT>(row_operand<ROWB>(db, qa, t2, ks), vreg[ks], dp[t2]);
+      }
+    mfma_read_pipeline<4 * NKS, 1, 4>();
+    // P = exp2(cs s - lse log2 e), dS = P (dP - D); masked pairs give 0.
+    uint32_t pw[2][2][4], dsw[2][2][4];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        float pv[2], ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int ii = i + e;
+          const int qi = qrow0 + t2 * 32 + 8 * (ii / 4) + 4 * hh + (ii % 4);
+          bool keep = qi < N;
+          if constexpr (CAUSAL) keep = keep && qi >= my_k;
+          // Rows 8 g + 4 hh .. +3 of tile t2, which the accumulator holds in
+          // its elements 4 g .. 4 g + 3.
+          const int row = t2 * 32 + 8 * (ii / 4) + 4 * hh + (ii % 4);
+          const float lse = lb[row];
+          const float dd = dlb[row];
+          pv[e] = keep ? __builtin_amdgcn_exp2f(fmaf(s[t2][ii], cs, -lse * kLog2e)) : 0.0f;
+          ds[e] = pv[e] * (dp[t2][ii] - dd);
+        }
+        pw[t2][i / 8][(i % 8) / 2] = pack2<DT>(pv[0], pv[1]);
+        dsw[t2][i / 8][(i % 8) / 2] = pack2<DT>(ds[0], ds[1]);
+      }
+    // dV^T += dO^T P, dK^T += Q^T dS.
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+          const u32x4 bp = {pw[t2][sg][0], pw[t2][sg][1], pw[t2][sg][2], pw[t2][sg][3]};
+          const u32x4 bs = {dsw[t2][sg][0], dsw[t2][sg][1], dsw[t2][sg][2], dsw[t2][sg][3]};
+          accv[t] = mfma16<DT>(tr_operand<ROWB>(db, qa, t, 2 * t2 + sg), bp, accv[t]);
+          acck[t] = mfma16<DT>(tr_operand<ROWB>(qb, qa, t, 2 * t2 + sg), bs, acck[t]);
+        }
+    mfma_read_pipeline<8 * NDT, 2, 4>();
+    bwd_barrier();
+  };
+  for (int j = 0; j < nblk; j += 2) {
+    step(j, q_lds0, do_lds0, lse_lds0, d_lds0, q_lds1, do_lds1, lse_lds1, d_lds1);
+    step(j + 1, q_lds1, do_lds1, lse_lds1, d_lds1, q_lds0, do_lds0, lse_lds0, d_lds0);
+  }
+
+  if (my_k < N) {
+    float* krow = p.dk + head_off + (int64_t)my_k * D;
+    float* vrow = p.dv + head_off + (int64_t)my_k * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = t * 32 + 8 * g + 4 * hh;
+        *reinterpret_cast<float4*>(krow + d0) =
+            float4{acck[t][4 * g] * p.scale, acck[t][4 * g + 1] * p.scale,
+                   acck[t][4 * g + 2] * p.scale, acck[t][4 * g + 3] * p.scale};
+        *reinterpret_cast<float4*>(vrow + d0) =
+            float4{accv[t][4 * g], accv[t][4 * g + 1], accv[t][4 * g + 2], accv[t][4 * g + 3]};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+
+bool aligned_b(const void* ptr, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(ptr) % a) == 0;
+}
+
+template <int DT, int D, bool CAUSAL>
+int launch_bwd_t(BwdParams prm, hipStream_t stream) {
+  prm.n_tiles = (prm.N + kBT - 1) / kBT;
+  void* args[] = {&prm};
+  const dim3 grid((unsigned)(prm.bh * prm.n_tiles));
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<DT, D, CAUSAL>),
+                                 grid, dim3(kBwdThreads), args, 0, stream);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL>), grid,
+                      dim3(kBwdThreads), args, 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int DT>
+int launch_bwd_dt(const BwdParams& prm, int d, int causal, hipStream_t s) {
+  if (d == 64)
+    return causal ? launch_bwd_t<DT, 64, true>(prm, s) : launch_bwd_t<DT, 64, false>(prm, s);
+  return causal ? launch_bwd_t<DT, 128, true>(prm, s) : launch_bwd_t<DT, 128, false>(prm, s);
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, float* dq, float* dk, float* dv, float* delta,
+                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                      int dtype, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (N > (int64_t)1 << 22 || B * H > (int64_t)1 << 24) return FA_ERR_SHAPE;
+  if (B * H * ((N + kBT - 1) / kBT) > INT32_MAX) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (!aligned_b(q, 16) || !aligned_b(k, 16) || !aligned_b(v, 16) || !aligned_b(o, 16) ||
+      !aligned_b(dout, 16) || !aligned_b(dq, 16) || !aligned_b(dk, 16) || !aligned_b(dv, 16) ||
+      !aligned_b(lse, 16) || !aligned_b(delta, 16))
+    return FA_ERR_ALIGN;
+  BwdParams prm;
+  prm.q = static_cast<const uint8_t*>(q);
+  prm.k = static_cast<const uint8_t*>(k);
+  prm.v = static_cast<const uint8_t*>(v);
+  prm.o = static_cast<const _Float16*>(o);
+  prm.lse = lse;
+  prm.dout = static_cast<const uint8_t*>(dout);
+  prm.dq = dq;
+  prm.dk = dk;
+  prm.dv = dv;
+  prm.delta = delta;
+  prm.N = (int)N;
+  prm.n_tiles = 0;
+  prm.bh = (int)(B * H);
+  prm.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == FA_DTYPE_BF16 ? launch_bwd_dt<FA_DTYPE_BF16>(prm, (int)d, causal, s)
+                                : launch_bwd_dt<FA_DTYPE_FP16>(prm, (int)d, causal, s);
+}

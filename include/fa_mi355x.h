@@ -122,6 +122,31 @@ int fa_fwd_ex(const void* q, const void* k, const void* v,
               int64_t B, int64_t H, int64_t N, int64_t d, float scale,
               int causal, int dtype, int layout, void* stream);
 
+/*
+ * fa_bwd -- gradients of the attention forward pass (fp16 or bf16 inputs,
+ * [B, H, N, d] layout).  Given dout = dL/dO for some loss L, it writes
+ *
+ *     dq = dL/dQ,  dk = dL/dK,  dv = dL/dV      (fp32 [B, H, N, d])
+ *     delta_i = sum_c dout_ic * o_ic              (fp32 [B, H, N])
+ *
+ * by the chain rule through O = P V, P = softmax(scale Q K^T [+ causal
+ * mask]): dV = P^T dO, dP = dO V^T, dS = P * (dP - delta), dQ = scale dS K,
+ * dK = scale dS^T Q.  P is recomputed block by block from lse, so the N x N
+ * matrices never reach device memory (the recomputation "TCA 51%，MFU 不足 8%"
+ * counts for the backward pass; the pages give no further detail of it).
+ * q, k, v, dout: the forward's inputs and the incoming gradient, element type
+ * dtype; o (fp16) and lse (fp32 [B, H, N]): the forward's outputs for the
+ * same q, k, v, scale and causal (fa_fwd's, or any consistent pair).  All
+ * pointers are device pointers, 16-byte aligned, none NULL when B*H*N > 0;
+ * the library allocates nothing (delta is the caller's workspace and an
+ * output).  dtype FP8 returns FA_ERR_DTYPE.  Two kernels are enqueued on the
+ * stream.  Returns FA_OK or a negative fa_status.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, float* dq, float* dk, float* dv,
+           float* delta, int64_t B, int64_t H, int64_t N, int64_t d,
+           float scale, int causal, int dtype, void* stream);
+
 /* Short English description of a status code (never NULL, static storage). */
 const char* fa_status_string(int status);
 

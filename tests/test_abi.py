@@ -166,3 +166,38 @@ def test_fa_fwd_ex_shape_limit_is_per_layout():
 def test_fa_fwd_ex_empty_is_a_noop(layout):
     assert _call_ex(layout=layout, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
     assert _call_ex(layout=layout, B=0) == 0
+
+
+def _call_bwd(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, do=A + 0x5000, dq=A + 0x6000, dk=A + 0x7000,
+                dv=A + 0x8000, delta=A + 0x9000, B=1, H=2, N=256, d=128, scale=0.1, causal=1,
+                dtype=0, stream=None)
+    args.update(kw)
+    return lib.fa_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"],
+                      args["dq"], args["dk"], args["dv"], args["delta"], args["B"], args["H"],
+                      args["N"], args["d"], args["scale"], args["causal"], args["dtype"],
+                      args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), "FA_ERR_DTYPE"),
+    (dict(dtype=7), "FA_ERR_DTYPE"),
+    (dict(d=32), "FA_ERR_HEAD_DIM"),
+    (dict(causal=3), "FA_ERR_CAUSAL"),
+    (dict(scale=-1.0), "FA_ERR_SCALE"),
+    (dict(N=-1), "FA_ERR_SHAPE"),
+    (dict(N=1 << 23), "FA_ERR_SHAPE"),
+    (dict(delta=None), "FA_ERR_NULL"),
+    (dict(dv=None), "FA_ERR_NULL"),
+    (dict(do=None), "FA_ERR_NULL"),
+    (dict(lse=L + 4), "FA_ERR_ALIGN"),
+    (dict(dk=A + 0x7008), "FA_ERR_ALIGN"),
+])
+def test_fa_bwd_rejects(kw, status):
+    assert _call_bwd(**kw) == _header_constants()[status]
+
+
+def test_fa_bwd_empty_is_a_noop():
+    assert _call_bwd(N=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None,
+                     dv=None, delta=None) == 0

@@ -1,0 +1,110 @@
+"""fa_bwd through the C ABI against the fp64 oracle's gradients.
+
+The GPU backward takes the GPU forward's O (fp16) and LSE, as a training step
+would; the oracle differentiates the exact problem.  Bars, relative to the
+size of each gradient tensor (R = the oracle's):
+  max|d - R| <= TOL_MAX * Mx   and   mean|d - R| <= TOL_MEAN * Mn,
+with Mx = max(max|R|, 0.1 G), Mn = max(mean|R|, 0.1 g), G and g the largest
+max|.| and mean|.| over the problem's three reference gradients: a gradient
+that vanishes exactly (dQ and dK at N = 1) is held to the problem's gradient
+scale instead of to zero.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from attention_forward_fa_amd import binding, inputs
+from oracle import attention as oracle
+from tests.test_gpu_parity import announce
+
+pytestmark = pytest.mark.gpu
+
+# (max, mean) relative bars per input type: 10 and 2 unit roundoffs of the
+# type P and dS are rounded to before the second products (fp16 2^-11,
+# bf16 2^-9); everything else is fp32.  Measured: about 0.5 u mean and up to
+# 1.5 u max.
+U = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -9}
+TOL = {k: (10 * u, 2 * u) for k, u in U.items()}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+def _up(bits, dtype):
+    raw = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+    return raw.view(binding.TORCH_DTYPES[dtype])
+
+
+def run_bwd(inp):
+    q, k, v, _ = binding.to_device(inp)
+    do = _up(inp.do, inp.dtype)
+    announce("bwd " + inp.describe())
+    o, lse = binding.fwd(q, k, v, causal=inp.causal, scale=inp.scale)
+    dq, dk, dv, delta = binding.bwd(q, k, v, o, lse, do, causal=inp.causal, scale=inp.scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv, delta, o
+
+
+def check_grads(inp, got, heads=None):
+    ref = oracle.run_bwd(inp, heads=heads)
+    BH = inp.B * inp.H
+    hsel = np.arange(BH) if heads is None else np.asarray(heads)
+    tmax, tmean = TOL[inp.dtype]
+    rec = {"case": "bwd " + inp.describe()}
+    msgs = []
+    gmax = max(np.abs(r).max() for r in ref)
+    gmean = max(np.abs(r).mean() for r in ref)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        g = g.cpu().numpy().astype(np.float64).reshape(BH, inp.N, inp.d)[hsel]
+        assert np.isfinite(g).all(), name
+        err = np.abs(g - r)
+        mx = err.max() / max(np.abs(r).max(), 0.1 * gmax)
+        mn = err.mean() / max(np.abs(r).mean(), 0.1 * gmean)
+        rec[name] = [float(mx), float(mn)]
+        msgs.append(f"{name} max {mx:.2e} mean {mn:.2e}")
+        assert mx <= tmax and mn <= tmean, f"{inp.describe()}: " + ", ".join(msgs)
+    announce(inp.describe() + ": " + ", ".join(msgs))
+    log = os.environ.get("FA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 100, 257])
+def test_bwd_small(dtype, d, causal, N):
+    inp = inputs.draw_bwd(2, 3, N, d, dtype, causal, seed=3000 + N + d)
+    dq, dk, dv, delta, o = run_bwd(inp)
+    check_grads(inp, (dq, dk, dv))
+    # delta = rowsum(dO * O) of the O the forward returned.
+    dov = torch.from_numpy(
+        oracle.decode_fp16(inp.do) if dtype == "fp16" else oracle.decode_bf16(inp.do))
+    want = (dov * o.cpu().double()).sum(-1)
+    assert torch.allclose(delta.cpu().double(), want, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype,causal", [("fp16", False), ("bf16", True)])
+def test_bwd_medium_sampled_heads(dtype, causal):
+    inp = inputs.draw_bwd(1, 8, 1500, 128, dtype, causal, seed=3100)
+    dq, dk, dv, _, _ = run_bwd(inp)
+    check_grads(inp, (dq, dk, dv), heads=[0, 5])
+
+
+def test_bwd_rejects_fp8():
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.float16, device="cuda")
+    lib = binding.load_library()
+    f = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
+    l = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
+    st = lib.fa_bwd(x.data_ptr(), x.data_ptr(), x.data_ptr(), x.data_ptr(), l.data_ptr(),
+                    x.data_ptr(), f.data_ptr(), f.data_ptr(), f.data_ptr(), l.data_ptr(),
+                    1, 1, 64, 64, 0.125, 0, 2, None)
+    assert binding.status_string(st) == "unknown dtype"
