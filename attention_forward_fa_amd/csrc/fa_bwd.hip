@@ -7,18 +7,18 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Two kernels, run in this order on the caller's stream:
+// Three kernel launches, in this order on the caller's stream:
 //   * fa_bwd_dq: one workgroup per (b, h, 128-query tile), a wave per 32
 //     queries, shaped like the forward: S^T = K Q^T and dP^T = V dO^T with Q
 //     and dO held in registers as B operands, dS^T in registers, then
 //     dQ^T += K^T dS^T with K^T read transposed (ds_read_b64_tr_b16) from the
 //     row-major K block in LDS.  It also computes D_i for its queries from O
 //     and dO and stores it (delta), for the second kernel.
-//   * fa_bwd_dkdv: one workgroup per (b, h, 128-key tile), a wave per 32
-//     keys held in registers (K and V rows as B operands): S = Q K^T and
-//     dP = dO V^T per 64-query block, then dV^T += dO^T P and
-//     dK^T += Q^T dS with dO^T and Q^T read transposed from the row-major
-//     dO and Q blocks.
+//   * fa_bwd_dkdv, twice (dV, then dK): one workgroup per (b, h, 128-key
+//     tile), a wave per 32 keys held in registers (K, and V for dK, rows as
+//     B operands): S = Q K^T (and dP = dO V^T) per 64-query block, then
+//     dV^T += dO^T P, or dK^T += Q^T dS, with dO^T / Q^T read transposed
+//     from the row-major dO / Q blocks.
 // Blocks stream global -> LDS (buffer_load ... lds, XOR-swizzled 16-byte
 // chunks) into two buffers, one barrier per block; the loops are unrolled by
 // two so each buffer is its own LDS array.  Rows past N read as zeros and are
@@ -195,7 +195,7 @@ __device__ __forceinline__ void bwd_barrier() {
 // dQ (and D = rowsum(dO * O)).
 // ---------------------------------------------------------------------------
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int ROWB = D * 2;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
@@ -279,7 +279,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
         st[t2] = mfma16<DT>(row_operand<ROWB>(kb, ka, t2, ks), qreg[ks], st[t2]);
         dpt[t2] = mfma16<DT>(row_operand<ROWB>(vb, ka, t2, ks), doreg[ks], dpt[t2]);
       }
-    mfma_read_pipeline<4 * NKS, 1, 4>();
+    mfma_read_pipeline<4 * NKS, 1, 2>();
+    __builtin_amdgcn_sched_barrier(0);
     // dS^T = P^T (dP^T - D), P^T = exp2(cs s - lse log2 e); masked pairs give 0.
     uint32_t dsw[2][2][4];
     const int kb0 = j * kBS;
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
         }
         dsw[t2][i / 8][(i % 8) / 2] = pack2<DT>(ds[0], ds[1]);
       }
+    __builtin_amdgcn_sched_barrier(0);
     // dQ^T += K^T dS^T.
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
           const u32x4 b = {dsw[t2][s][0], dsw[t2][s][1], dsw[t2][s][2], dsw[t2][s][3]};
           acc[t] = mfma16<DT>(tr_operand<ROWB>(kb, ka, t, 2 * t2 + s), b, acc[t]);
         }
-    mfma_read_pipeline<4 * NDT, 2, 4>();
+    mfma_read_pipeline<4 * NDT, 2, 2>();
     bwd_barrier();
   };
   for (int j = 0; j < nblk; j += 2) {
@@ -331,10 +333,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV.
+// dK and dV.  PART 1 computes dV alone (S, P, dV^T += dO^T P), PART 2 dK
+// alone (S, dP, dS, dK^T += Q^T dS): recomputing S twice costs one product
+// more than both in one kernel, but each half fits two waves per SIMD in
+// the register file, where the fused kernel runs one.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
+template <int DT, int D, bool CAUSAL, int PART>
+__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p) {
+  static_assert(PART == 1 || PART == 2, "dV (1) or dK (2)");
+  constexpr bool kDV = PART == 1;
   constexpr int ROWB = D * 2;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
@@ -381,7 +388,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p
   for (int ks = 0; ks < NKS; ++ks) {
     const int byte = my_k * ROWB + (ks * 16 + 8 * hh) * 2;
     kreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(krs, byte, 0, 0);
-    vreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(vrs, byte, 0, 0);
+    if constexpr (!kDV) vreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(vrs, byte, 0, 0);
   }
 
   BlockAddr<ROWB> qa;
@@ -394,12 +401,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p
   const int qb_begin = CAUSAL ? (k0 / kBS) : 0;
   const int nblk = (N - qb_begin * kBS + kBS - 1) / kBS;
 
-  f32x16 acck[NDT], accv[NDT];
+  f32x16 acc[NDT];  // dV^T (PART 1) or dK^T (PART 2)
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
-    acck[t] = f32x16{};
-    accv[t] = f32x16{};
-  }
+  for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
 
   // LSE and D rows of a block: wave 0 and wave 1, one dword per lane.
   auto load_ld = [&](float* lse_dst, float* d_dst, int row0) __attribute__((always_inline)) {
@@ -430,11 +434,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         s[t2] = mfma16<DT>(row_operand<ROWB>(qb, qa, t2, ks), kreg[ks], s[t2]);
-        dp[t2] = mfma16<DT>(row_operand<ROWB>(db, qa, t2, ks), vreg[ks], dp[t2]);
+        if constexpr (!kDV)
+          dp[t2] = mfma16<DT>(row_operand<ROWB>(db, qa, t2, ks), vreg[ks], dp[t2]);
       }
-    mfma_read_pipeline<4 * NKS, 1, 4>();
+    mfma_read_pipeline<(kDV ? 2 : 4) * NKS, 1, 4>();
+    __builtin_amdgcn_sched_barrier(0);
     // P = exp2(cs s - lse log2 e), dS = P (dP - D); masked pairs give 0.
-    uint32_t pw[2][2][4], dsw[2][2][4];
+    // w holds P (PART 1) or dS (PART 2) as pairs of the input type.
+    uint32_t w[2][2][4];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -450,26 +457,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p
           // its elements 4 g .. 4 g + 3.
           const int row = t2 * 32 + 8 * (ii / 4) + 4 * hh + (ii % 4);
           const float lse = lb[row];
-          const float dd = dlb[row];
           pv[e] = keep ? __builtin_amdgcn_exp2f(fmaf(s[t2][ii], cs, -lse * kLog2e)) : 0.0f;
-          ds[e] = pv[e] * (dp[t2][ii] - dd);
+          if constexpr (!kDV) ds[e] = pv[e] * (dp[t2][ii] - dlb[row]);
         }
-        pw[t2][i / 8][(i % 8) / 2] = pack2<DT>(pv[0], pv[1]);
-        dsw[t2][i / 8][(i % 8) / 2] = pack2<DT>(ds[0], ds[1]);
+        w[t2][i / 8][(i % 8) / 2] = kDV ? pack2<DT>(pv[0], pv[1]) : pack2<DT>(ds[0], ds[1]);
       }
-    // dV^T += dO^T P, dK^T += Q^T dS.
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P, or dK^T += Q^T dS.
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
         for (int t = 0; t < NDT; ++t) {
-          const u32x4 bp = {pw[t2][sg][0], pw[t2][sg][1], pw[t2][sg][2], pw[t2][sg][3]};
-          const u32x4 bs = {dsw[t2][sg][0], dsw[t2][sg][1], dsw[t2][sg][2], dsw[t2][sg][3]};
-          accv[t] = mfma16<DT>(tr_operand<ROWB>(db, qa, t, 2 * t2 + sg), bp, accv[t]);
-          acck[t] = mfma16<DT>(tr_operand<ROWB>(qb, qa, t, 2 * t2 + sg), bs, acck[t]);
+          const u32x4 b = {w[t2][sg][0], w[t2][sg][1], w[t2][sg][2], w[t2][sg][3]};
+          acc[t] = mfma16<DT>(tr_operand<ROWB>(kDV ? db : qb, qa, t, 2 * t2 + sg), b, acc[t]);
         }
-    mfma_read_pipeline<8 * NDT, 2, 4>();
+    mfma_read_pipeline<4 * NDT, 2, 4>();
     bwd_barrier();
   };
   for (int j = 0; j < nblk; j += 2) {
@@ -478,18 +482,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p
   }
 
   if (my_k < N) {
-    float* krow = p.dk + head_off + (int64_t)my_k * D;
-    float* vrow = p.dv + head_off + (int64_t)my_k * D;
+    float* row = (kDV ? p.dv : p.dk) + head_off + (int64_t)my_k * D;
+    const float f = kDV ? 1.0f : p.scale;
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = t * 32 + 8 * g + 4 * hh;
-        *reinterpret_cast<float4*>(krow + d0) =
-            float4{acck[t][4 * g] * p.scale, acck[t][4 * g + 1] * p.scale,
-                   acck[t][4 * g + 2] * p.scale, acck[t][4 * g + 3] * p.scale};
-        *reinterpret_cast<float4*>(vrow + d0) =
-            float4{accv[t][4 * g], accv[t][4 * g + 1], accv[t][4 * g + 2], accv[t][4 * g + 3]};
+        *reinterpret_cast<float4*>(row + d0) =
+            float4{acc[t][4 * g] * f, acc[t][4 * g + 1] * f, acc[t][4 * g + 2] * f,
+                   acc[t][4 * g + 3] * f};
       }
   }
 }
@@ -510,8 +512,11 @@ int launch_bwd_t(BwdParams prm, hipStream_t stream) {
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<DT, D, CAUSAL>),
                                  grid, dim3(kBwdThreads), args, 0, stream);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL>), grid,
-                      dim3(kBwdThreads), args, 0, stream);
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL, 1>),
+                      grid, dim3(kBwdThreads), args, 0, stream);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL, 2>),
+                      grid, dim3(kBwdThreads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -42,6 +42,9 @@ def parse_args(argv=None):
     ap.add_argument("--layout", default="bhnd", choices=["bhnd", "bnhd"],
                     help="tensor layout of q, k, v, o: [B,H,N,d] (fa_fwd) or [B,N,H,d] "
                          "(fa_fwd_ex)")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="time the forward pass (default) or the backward pass (fa_bwd, "
+                         "fp16/bf16 workloads; counted FLOPs 10*B*H*N^2*d, halved if causal)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,6 +162,38 @@ def time_gpu(inp, steps, warmup, clock=None, layout="bhnd"):
     return sec
 
 
+def time_gpu_bwd(inp, steps, warmup):
+    """Average seconds per fa_bwd call (the forward's O and LSE computed once
+    beforehand), HIP events on the launch stream."""
+    import torch
+
+    from attention_forward_fa_amd import binding
+
+    if inp.dtype not in ("fp16", "bf16"):
+        raise SystemExit("the backward pass takes fp16 or bf16 workloads")
+    q, k, v, _ = binding.to_device(inp, "cuda")
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(inp.seed or 0)).to(
+        q.dtype).to("cuda")
+    o, lse = binding.fwd(q, k, v, causal=inp.causal, scale=inp.scale)
+    torch.cuda.synchronize()
+
+    def step():
+        binding.bwd(q, k, v, o, lse, do, causal=inp.causal, scale=inp.scale)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / steps
+
+
 def cpu_baseline(inp, budget_s):
     """The oracle, as it stands, on whole heads of the workload until the budget runs out."""
     import threadpoolctl
@@ -236,6 +271,22 @@ def main(argv=None):
         return copy_calibration(args.copy_calibration, args.steps)
     name, B, H, N, d, dtype, causal, seed = inputs.config(args.workload)
     inp = inputs.draw(B, H, N, d, dtype, causal, seed)
+    if args.which == "bwd":
+        # Backward pass: 5 products of 2*N^2*d per head (2.5x the forward count).
+        steps, warmup = min(args.steps, 200), min(args.warmup, 100)
+        sec = time_gpu_bwd(inp, steps, warmup)
+        flops = 2.5 * acc.counted_flops(B, H, N, d, causal)
+        tf = flops / sec / 1e12
+        peak = acc.PEAK_TFLOPS[dtype]
+        print(json.dumps({
+            "metric": "attention bwd TFLOPS (10BHN²d/t, halved if causal), 1 GPU",
+            "value": round(tf, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+            "dtype": {"fp16": "f16", "bf16": "bf16"}[dtype], "data": "synthetic",
+            "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "input_dtype": dtype,
+                       "causal": bool(causal), "gradients": "fp32"},
+            "frac_of_peak": round(tf / peak, 4)}), flush=True)
+        return 0
     clock = ClockSampler()
     sec = time_gpu(inp, args.steps, args.warmup, clock, args.layout)
     flops, tf, peak = describe(inp, sec)
