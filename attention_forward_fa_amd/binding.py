@@ -35,6 +35,8 @@ SIGNATURES = {
                                   ctypes.c_float, ctypes.c_int, _P]),
     "fa_fwd_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                  ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]),
+    "fa_fwd_fp8_pv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, _I64, _P]),
     "fa_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                               ctypes.c_float, ctypes.c_int, ctypes.c_int, _P]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -171,6 +173,28 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, descale_q: torch.
     return out, lse
 
 
+def _layout_shape(q, layout):
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    if layout == "bnhd":
+        B, N, H, d = q.shape
+    else:
+        B, H, N, d = q.shape
+    return B, H, N, d
+
+
+def _descale_ptrs(q, descales, B, H):
+    if descales is None:
+        return None, None, None
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError("descales apply to float8_e4m3fn inputs only")
+    for t in descales:
+        if (t.dtype != torch.float32 or t.numel() != B * H or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError("descales must be contiguous float32 device tensors of B*H values")
+    return descales
+
+
 def fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bhnd",
            causal: bool = False, scale: Optional[float] = None,
            descales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
@@ -178,22 +202,9 @@ def fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bhn
            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """fa_fwd_ex: q, k, v, out in [B, H, N, d] ("bhnd") or [B, N, H, d] ("bnhd");
     lse is [B, H, N] either way.  descales (fp8 only): float32 [B*H] each."""
-    if layout not in LAYOUTS:
-        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    B, H, N, d = _layout_shape(q, layout)
     _validate(q, k, v)
-    if layout == "bnhd":
-        B, N, H, d = q.shape
-    else:
-        B, H, N, d = q.shape
-    dq = dk = dv = None
-    if descales is not None:
-        if q.dtype != torch.float8_e4m3fn:
-            raise TypeError("descales apply to float8_e4m3fn inputs only")
-        for t in descales:
-            if (t.dtype != torch.float32 or t.numel() != B * H or not t.is_contiguous()
-                    or t.device != q.device):
-                raise ValueError("descales must be contiguous float32 device tensors of B*H values")
-        dq, dk, dv = descales
+    dq, dk, dv = _descale_ptrs(q, descales, B, H)
     out, lse = _outputs(q, out, lse, layout)
     scale = _default_scale(d) if scale is None else float(scale)
     lib = load_library()
@@ -202,6 +213,30 @@ def fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bhn
         st = lib.fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(out),
                            _ptr(lse), B, H, N, d, scale, int(bool(causal)),
                            _TORCH_DTYPE_CODE[q.dtype], LAYOUTS[layout], stream)
+    _check(st)
+    return out, lse
+
+
+def fwd_fp8_pv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, min_keys: int = 512,
+               layout: str = "bhnd", causal: bool = False, scale: Optional[float] = None,
+               descales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+               out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fa_fwd_fp8_pv: fwd_ex for float8_e4m3fn q, k, v with P V on the fp8 matrix
+    instructions for the query tiles whose first row sees at least min_keys keys."""
+    B, H, N, d = _layout_shape(q, layout)
+    _validate(q, k, v)
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError("fwd_fp8_pv takes float8_e4m3fn q, k, v")
+    dq, dk, dv = _descale_ptrs(q, descales, B, H)
+    out, lse = _outputs(q, out, lse, layout)
+    scale = _default_scale(d) if scale is None else float(scale)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_fwd_fp8_pv(_ptr(q), _ptr(k), _ptr(v), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(out), _ptr(lse), B, H, N, d, scale, int(bool(causal)),
+                               LAYOUTS[layout], int(min_keys), stream)
     _check(st)
     return out, lse
 

@@ -114,6 +114,14 @@ __device__ __forceinline__ f32x16 mfma_qk(const QKOperand<DT>& a, const QKOperan
   }
 }
 
+// O^T += V^T P^T on the fp8 matrix cores: A = 32 e4m3 values of V^T per lane,
+// B = 32 e4m3 probabilities per lane, each lane's B values multiplied by
+// 2^(sb - 127) (an E8M0 exponent; one per lane, i.e. per query and half of the
+// 64-key contraction).
+__device__ __forceinline__ f32x16 mfma_pv8(const i32x8& a, const i32x8& b, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
+
 
 
 
@@ -141,12 +149,13 @@ __device__ __forceinline__ void mfma_read_valu_pipeline() {
 // instructions and TPM transcendental ones (v_exp_f32 and the like form a
 // class of their own for the scheduler); after MFMAs 3 .. 3+NW-1 one LDS
 // write each, and after MFMAs
-// 5 .. 5+NVM-1 one global load each, so the staging of the next block hides
-// behind the matrix work too.
-template <int NA, int RA, int NB, int RB, int LA, int VPM, int TPM, int NW, int NVM, int I = 0>
+// VM0 .. VM0+NVM-1 one global load each, so the staging of the next block
+// hides behind the matrix work too.
+template <int NA, int RA, int NB, int RB, int LA, int VPM, int TPM, int NW, int NVM, int VM0 = 5,
+          int I = 0>
 __device__ __forceinline__ void mfma_run_pipeline() {
   constexpr int NM = NA + NB;
-  static_assert(LA <= NM && 5 + NVM <= NM, "run too short");
+  static_assert(LA <= NM && VM0 + NVM <= NM, "run too short");
   if constexpr (I == 0)  // reads of the first LA MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, LA <= NA ? LA * RA : NA * RA + (LA - NA) * RB, 0);
   if constexpr (I < NM) {
@@ -154,10 +163,10 @@ __device__ __forceinline__ void mfma_run_pipeline() {
     if constexpr (I + LA < NM)
       __builtin_amdgcn_sched_group_barrier(0x100, I + LA < NA ? RA : RB, 0);  // reads of I+LA
     if constexpr (I >= 3 && I < 3 + NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    if constexpr (I >= 5 && I < 5 + NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if constexpr (I >= VM0 && I < VM0 + NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
     __builtin_amdgcn_sched_group_barrier(0x400, TPM, 0);  // transcendental
-    mfma_run_pipeline<NA, RA, NB, RB, LA, VPM, TPM, NW, NVM, I + 1>();
+    mfma_run_pipeline<NA, RA, NB, RB, LA, VPM, TPM, NW, NVM, VM0, I + 1>();
   }
 }
 
@@ -194,6 +203,7 @@ struct Params {
   int n_qtiles;
   int bh;      // B*H
   int layout;  // FA_LAYOUT_BHND or FA_LAYOUT_BNHD (q, k, v and o alike)
+  int qt_base; // first query tile of this launch (n_qtiles tiles from there)
   float scale;
 };
 
@@ -201,7 +211,23 @@ struct Params {
 
 
 
-template <int DT, int D, bool CAUSAL, int WAVES>
+// Swizzle of the fp8 V rows that the P V operand reads with
+// ds_read_b64_tr_b8 (the 16-byte chunk XOR, from the row's place inside its
+// group of 16 keys).  Those reads take, per half wave, the rows of one half
+// of a 16-key group (keys 0-3 and 8-11, or 4-7 and 12-15) at the two chunks of
+// 32 d values; with rows of 128 bytes an even and an odd row sit 64 banks
+// apart, so the four rows of each parity need four distinct even XORs; with
+// rows of 64 bytes rows r and r+8 meet and differ by an XOR of 2.
+template <int ROWB>
+__device__ __forceinline__ int vswz8(int row) {
+  if constexpr (ROWB == 128) return (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
+  else return ((row >> 3) & 1) << 1;
+}
+
+// PV8: fp8 inputs with P V on the fp8 matrix cores too (V kept as e4m3 in
+// LDS, P rounded to e4m3 under a per-row power-of-two scale); otherwise P V
+// runs in fp16.
+template <int DT, int D, bool CAUSAL, int WAVES, bool PV8 = false>
 __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int kWaves = Shape<WAVES>::waves;
@@ -224,6 +250,9 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   constexpr int VD = kBC * D / (4 * kThreads);  // d values per staging thread (4 keys each)
   constexpr int VIN = VD * ES;            // input bytes per key row per staging thread
   static_assert(kBC * D == 4 * VD * kThreads, "V staging must tile the workgroup");
+  static_assert(!PV8 || (DT == FA_DTYPE_FP8_E4M3 && WAVES == 4), "fp8 P V: fp8, four waves");
+  // fp16 P V: two V^T stages; fp8 P V: four stages of V rows as loaded.
+  constexpr int VSTAGE = PV8 ? KBUF : VBUF;
 
   // Four K stages (K is loaded three blocks ahead of its use) and two V^T
   // stages, each an array of its own: the compiler can then tell the buffer
@@ -233,8 +262,10 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   __shared__ __attribute__((aligned(16))) uint8_t k_lds1[KBUF];
   __shared__ __attribute__((aligned(16))) uint8_t k_lds2[KBUF];
   __shared__ __attribute__((aligned(16))) uint8_t k_lds3[KBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds0[VBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds1[VBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds0[VSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds1[VSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds2[PV8 ? KBUF : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds3[PV8 ? KBUF : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -245,6 +276,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   // ---- work decomposition: one workgroup per (b*H + h, query tile) ----------
   int bh, qt;
   tile_of(blockIdx.x, p.bh, p.n_qtiles, CAUSAL, bh, qt);
+  qt += p.qt_base;
   const int N = p.N;
   // Element offset of the head's first row and the stride between its rows:
   // [B, H, N, d] (rows of one head adjacent) or [B, N, H, d] (rows of one head
@@ -318,6 +350,14 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     const int row = slot / KCPR, phys = slot % KCPR;
     k_goff[u] = row * GRS + ((phys ^ swz<KROWB>(row)) * 16);
   }
+  // fp8 P V: V rows go global -> LDS the same way, under their own swizzle.
+  int v8_goff[K_PER_W];
+#pragma unroll
+  for (int u = 0; u < K_PER_W; ++u) {
+    const int slot = (u * kWaves + wave) * kWave + lane;
+    const int row = slot / KCPR, phys = slot % KCPR;
+    v8_goff[u] = row * GRS + ((phys ^ vswz8<KROWB>(row)) * 16);
+  }
   const int vquad = tid % 16, vdgrp = tid / 16;
   const int v_goff = 4 * vquad * GRS + vdgrp * VIN;
   int v_loff;
@@ -339,6 +379,14 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     for (int u = 0; u < K_PER_W; ++u) {
       const int inst = u * kWaves + wave;
       buffer_to_lds16(krs, kbuf + inst * kWave * 16, k_goff[u] + boff, 0);
+    }
+  };
+  auto load_v8 = [&](int kb, uint8_t* vbuf) __attribute__((always_inline)) {
+    const int boff = block_off(kb);
+#pragma unroll
+    for (int u = 0; u < K_PER_W; ++u) {
+      const int inst = u * kWaves + wave;
+      buffer_to_lds16(vrs, vbuf + inst * kWave * 16, v8_goff[u] + boff, 0);
     }
   };
   auto load_v = [&](int kb, VRegs& vst) __attribute__((always_inline)) {
@@ -406,6 +454,21 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   // V^T (A operand of O^T = V^T P^T): row t*32 + lr, the 8 contiguous key
   // positions 16*s + 8*hh .. +7 of key tile kt.
   const int vt_raddr = lr * VTROW + 16 * hh;
+  // fp8 P V: the A operand (32 e4m3 values of V^T per lane) comes from the
+  // row-major V block through four ds_read_b64_tr_b8.  In each group of 16
+  // lanes, lane 2e+h gives the address of 8 bytes (columns 8h .. 8h+7 of a
+  // 16-byte span) of row e of an 8 x 16-byte tile and lane L receives column L
+  // of the tile's 8 rows.  Group g reads d columns t*32 + 16*(g&1) .. +15, and
+  // in read r the rows are the keys behind bytes 8r .. 8r+7 of the B operand
+  // of half g>>1: key 16r + 8*(e>>2) + 4*(g>>1) + (e&3).
+  int vt8_addr[NDT];
+  {
+    const int g = lane >> 4, li = lane & 15, e = li >> 1;
+    const int b = 8 * (e >> 2) + 4 * (g >> 1) + (e & 3);  // row inside its 16-key group
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+      vt8_addr[t] = b * KROWB + (((2 * t + (g & 1)) ^ vswz8<KROWB>(b)) * 16) + 8 * (li & 1);
+  }
 
   // ---- running softmax state and the O^T accumulator --------------------------
   f32x16 acc[NDT];
@@ -419,6 +482,9 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   float l_run = 0.0f;  // this lane's share of the row sum, relative to m_run
   // P as fp16 pairs, the B operand of O^T += V^T P^T: [key tile][k-step][dword].
   typedef uint32_t PRegs[2][2][4];
+  // fp8 P V: P as 32 e4m3 codes (byte 16*kt + i = accumulator element i of key
+  // tile kt), then the E8M0 exponent of the scale 2^-k they were taken under.
+  typedef uint32_t P8Regs[9];
 
   // S^T = K Q^T for the block in K buffer kbuf: two 32-key tiles.  The tiles
   // alternate so consecutive MFMAs are independent.
@@ -523,6 +589,76 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
         }
   };
 
+  // fp8 P V softmax: as above, except that the probabilities of a row are
+  // taken as 2^k exp2(c s - c m) with k = 8 - ceil(c (block max - m)), which
+  // lifts the block's largest one into (2^7, 2^8] (e4m3 holds 3 fraction bits
+  // from 2^-6 to 448), rounded to e4m3, and the MFMA scales them back by 2^-k.
+  // The row sum takes the unrounded values.
+  auto softmax8 = [&](f32x16* st, P8Regs& pw, bool& rescale) __attribute__((always_inline)) -> float {
+    float m0 = st[0][0], m1 = st[1][0];
+#pragma unroll
+    for (int i = 1; i < 15; i += 2) {
+      m0 = vmax(vmax(m0, st[0][i]), st[0][i + 1]);
+      m1 = vmax(vmax(m1, st[1][i]), st[1][i + 1]);
+    }
+    const float mx = max_pair32(vmax(vmax(m0, st[0][15]), vmax(m1, st[1][15])));
+    rescale = __builtin_amdgcn_ballot_w64((mx - m_run) * c > kRescaleLog2) != 0;
+    const float m_use = rescale ? vmax(m_run, mx) : m_run;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
+    m_run = m_use;
+    // (mx - m_use) c <= kRescaleLog2 = 8, so k >= 0; a row with no key in the
+    // block (mx = -inf) takes k = 64.
+    const float kf = fminf(8.0f - ceilf((mx - m_use) * c), 64.0f);
+    const int ki = (int)kf;
+    const float bias = fmaf(-m_use, c, kf);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = fmaf(st[kt][i], c, bias);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = __builtin_amdgcn_exp2f(st[kt][i]);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kt = w / 4, g = w % 4;
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(st[kt][4 * g], st[kt][4 * g + 1], 0, false);
+      pw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(st[kt][4 * g + 2], st[kt][4 * g + 3], lo,
+                                                        true);
+    }
+    pw[8] = (uint32_t)(127 - ki);
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part[i % 4] += st[kt][i];
+    l_run = l_run * alpha +
+            __builtin_amdgcn_ldexpf((part[0] + part[1]) + (part[2] + part[3]), -ki);
+    return alpha;
+  };
+
+  // fp8 P V: one MFMA per d tile covers the whole 64-key block; byte j of a
+  // lane's B operand is key 32*(j/16) + 8*((j%16)/4) + 4*hh + (j%4), the key
+  // the tr_b8 reads put in byte j of the A operand.
+  auto pv8 = [&](const uint8_t* vbuf, const P8Regs& pw) __attribute__((always_inline)) {
+    i32x8 b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = (int)pw[i];
+    const int sb = (int)pw[8];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      i32x8 a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2_t*)(vbuf + vt8_addr[t] + r * 16 * KROWB));
+        a[2 * r] = x[0];
+        a[2 * r + 1] = x[1];
+      }
+      acc[t] = mfma_pv8(a, b, sb, acc[t]);
+    }
+  };
+
   // ---- software pipeline ---------------------------------------------------------
   // Iteration j writes V(j) -- loaded into registers during iteration j-1 --
   // to V^T buffer j&1 (last read in iteration j-1), loads V(j+1) into the
@@ -539,80 +675,164 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   // counts are fixed; the QK^T of the block after the last is computed and
   // discarded, and iteration 0 multiplies a zero P(-1) with the zeroed V^T
   // buffer 1.
-  for (int i = tid; i < VBUF / 16; i += kThreads) {
-    reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0u, 0u, 0u, 0u};
-    reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  constexpr int NVM = K_PER_W + 4;  // global load instructions per wave per iteration
-  load_k(0, k_lds0);
-  load_k(kBC, k_lds1);
-  load_v(0, vst);
-  load_k(2 * kBC, k_lds2);
-  // This wave's K(0) and K(1) have landed; V(0) and K(2) may still fly.
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 + K_PER_W) : "memory");
-  barrier();
-
-  f32x16 sa[2], sb[2];
-  PRegs pa, pb = {};
-  qk(k_lds0, sa);
-  barrier();
-
-  constexpr int NPV = NDT * 4;     // P V MFMAs per block
-  constexpr int NQK = 2 * NKS;     // QK^T MFMAs per block
-  constexpr int VPM = (160 + NPV + NQK - 1) / (NPV + NQK);  // about 160 VALU per block
-  constexpr int TPM = (kBC / 2 + NPV + NQK) / (NPV + NQK);  // kBC / 2 + 1 exponentials per block
-  auto step = [&](int j, const uint8_t* k_next, uint8_t* k_fill, const uint8_t* v_prev,
-                  uint8_t* v_fill, f32x16* s_cur, f32x16* s_next, PRegs& p_cur,
-                  const PRegs& p_prev) __attribute__((always_inline)) {
-    if (needs_mask(j)) mask(s_cur, j * kBC);
-    store_v(vst, v_fill);             // V(j) -> V^T
-    load_v((j + 1) * kBC, vst);       // V(j+1) -> registers
-    // V(j+1) goes out before K(j+3): the wait for V(j+1) where it is stored
-    // then leaves K(j+3) in flight.
-    __builtin_amdgcn_sched_barrier(0);
-    load_k((j + 3) * kBC, k_fill);    // K(j+3)
-    pv(v_prev, p_prev);               // P V of block j-1
-    qk(k_next, s_next);               // QK^T of block j+1
-    bool rescale;
-    const float alpha = softmax(s_cur, p_cur, rescale);
-    mfma_run_pipeline<NPV, 1, NQK, KCH, 4, VPM, TPM, 0, K_PER_W>();
-    // Keep the softmax in this block, beside the MFMAs: its results are only
-    // used next iteration, and the compiler would otherwise sink it there.
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) asm volatile("" ::"v"(p_cur[kt][s][w]));
-    asm volatile("" ::"v"(l_run));
-    if (rescale) {  // after P V(j-1): all of O^T is relative to the old max
-#pragma unroll
-      for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
+  if constexpr (!PV8) {
+    for (int i = tid; i < VBUF / 16; i += kThreads) {
+      reinterpret_cast<u32x4*>(v_lds0)[i] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0u, 0u, 0u, 0u};
     }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVM) : "memory");
+    constexpr int NVM = K_PER_W + 4;  // global load instructions per wave per iteration
+    load_k(0, k_lds0);
+    load_k(kBC, k_lds1);
+    load_v(0, vst);
+    load_k(2 * kBC, k_lds2);
+    // This wave's K(0) and K(1) have landed; V(0) and K(2) may still fly.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 + K_PER_W) : "memory");
     barrier();
-  };
-  // Iteration j with j % 4 == 0, 1, 2, 3.
-  auto step0 = [&](int j) __attribute__((always_inline)) { step(j, k_lds1, k_lds3, v_lds1, v_lds0, sa, sb, pa, pb); };
-  auto step1 = [&](int j) __attribute__((always_inline)) { step(j, k_lds2, k_lds0, v_lds0, v_lds1, sb, sa, pb, pa); };
-  auto step2 = [&](int j) __attribute__((always_inline)) { step(j, k_lds3, k_lds1, v_lds1, v_lds0, sa, sb, pa, pb); };
-  auto step3 = [&](int j) __attribute__((always_inline)) { step(j, k_lds0, k_lds2, v_lds0, v_lds1, sb, sa, pb, pa); };
-  auto last_pv = [&](const uint8_t* vbuf, const PRegs& p_last) __attribute__((always_inline)) {
+
+    f32x16 sa[2], sb[2];
+    PRegs pa, pb = {};
+    qk(k_lds0, sa);
+    barrier();
+
+    constexpr int NPV = NDT * 4;     // P V MFMAs per block
+    constexpr int NQK = 2 * NKS;     // QK^T MFMAs per block
+    constexpr int VPM = (160 + NPV + NQK - 1) / (NPV + NQK);  // about 160 VALU per block
+    constexpr int TPM = (kBC / 2 + NPV + NQK) / (NPV + NQK);  // kBC / 2 + 1 exponentials per block
+    auto step = [&](int j, const uint8_t* k_next, uint8_t* k_fill, const uint8_t* v_prev,
+                    uint8_t* v_fill, f32x16* s_cur, f32x16* s_next, PRegs& p_cur,
+                    const PRegs& p_prev) __attribute__((always_inline)) {
+      if (needs_mask(j)) mask(s_cur, j * kBC);
+      store_v(vst, v_fill);             // V(j) -> V^T
+      load_v((j + 1) * kBC, vst);       // V(j+1) -> registers
+      // V(j+1) goes out before K(j+3): the wait for V(j+1) where it is stored
+      // then leaves K(j+3) in flight.
+      __builtin_amdgcn_sched_barrier(0);
+      load_k((j + 3) * kBC, k_fill);    // K(j+3)
+      pv(v_prev, p_prev);               // P V of block j-1
+      qk(k_next, s_next);               // QK^T of block j+1
+      bool rescale;
+      const float alpha = softmax(s_cur, p_cur, rescale);
+      mfma_run_pipeline<NPV, 1, NQK, KCH, 4, VPM, TPM, 0, K_PER_W>();
+      // Keep the softmax in this block, beside the MFMAs: its results are only
+      // used next iteration, and the compiler would otherwise sink it there.
+  #pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+  #pragma unroll
+        for (int s = 0; s < 2; ++s)
+  #pragma unroll
+          for (int w = 0; w < 4; ++w) asm volatile("" ::"v"(p_cur[kt][s][w]));
+      asm volatile("" ::"v"(l_run));
+      if (rescale) {  // after P V(j-1): all of O^T is relative to the old max
+  #pragma unroll
+        for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
+      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVM) : "memory");
+      barrier();
+    };
+    // Iteration j with j % 4 == 0, 1, 2, 3.
+    auto step0 = [&](int j) __attribute__((always_inline)) { step(j, k_lds1, k_lds3, v_lds1, v_lds0, sa, sb, pa, pb); };
+    auto step1 = [&](int j) __attribute__((always_inline)) { step(j, k_lds2, k_lds0, v_lds0, v_lds1, sb, sa, pb, pa); };
+    auto step2 = [&](int j) __attribute__((always_inline)) { step(j, k_lds3, k_lds1, v_lds1, v_lds0, sa, sb, pa, pb); };
+    auto step3 = [&](int j) __attribute__((always_inline)) { step(j, k_lds0, k_lds2, v_lds0, v_lds1, sb, sa, pb, pa); };
+    auto last_pv = [&](const uint8_t* vbuf, const PRegs& p_last) __attribute__((always_inline)) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS load outlives the loop
+      pv(vbuf, p_last);
+      mfma_read_pipeline<NPV, 1, (NPV < 8 ? NPV : 8)>();
+    };
+    // The loop runs to the next multiple of four blocks: blocks past the last
+    // one are fully masked (keys past N, or causal keys after every query of the
+    // workgroup), so they change neither m, l nor O.  One copy of the loop body
+    // keeps the register allocation of the steady state.
+    for (int j = 0; j < nblk; j += 4) {
+      step0(j);
+      step1(j + 1);
+      step2(j + 2);
+      step3(j + 3);
+    }
+    last_pv(v_lds1, pb);  // the last iteration is odd: P in pb, V^T in buffer 1
+  } else {
+    // fp8 P V: V(j+2) goes global -> LDS in iteration j into V stage (j+2)%4,
+    // which held V(j-2), read in iteration j-1; P V of block j-1 reads stage
+    // (j-1)%4.  Otherwise the iteration is the one above, without the V^T
+    // store.  Stage 3 starts zeroed for the P V of the zero block -1 (e4m3
+    // bytes 0x7f / 0xff are NaN, and 0 * NaN would be NaN).
+    for (int i = tid; i < KBUF / 16; i += kThreads)
+      reinterpret_cast<u32x4*>(v_lds3)[i] = u32x4{0u, 0u, 0u, 0u};
+    constexpr int NVM8 = 2 * K_PER_W;  // global load instructions per wave per iteration
+    load_k(0, k_lds0);
+    load_v8(0, v_lds0);
+    load_k(kBC, k_lds1);
+    load_v8(kBC, v_lds1);
+    load_k(2 * kBC, k_lds2);
+    // This wave's K(0), V(0) and K(1) have landed; V(1) and K(2) may still fly.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVM8) : "memory");
+    barrier();
+
+    f32x16 sa[2], sb[2];
+    P8Regs pa, pb = {};
+    pb[8] = 127u;
+    qk(k_lds0, sa);
+    barrier();
+
+    constexpr int NQK = 2 * NKS;     // QK^T MFMAs per block (one P V MFMA per d tile)
+    constexpr int NM8 = NDT + NQK;
+    constexpr int VPM8 = (140 + NM8 - 1) / NM8;          // about 140 VALU per block
+    constexpr int TPM8 = (kBC / 2 + 1 + NM8 - 1) / NM8;  // kBC / 2 + 1 exponentials
+    constexpr int VM08 = (NM8 - NVM8) / 2;
+    // The O^T rescale a block's softmax asks for is applied at the top of the
+    // next iteration, just before the P V it must precede: a branch after the
+    // MFMA run would let the compiler sink that run's QK^T MFMAs behind it.
+    bool resc_prev = false;
+    float alpha_prev = 1.0f;
+    auto step8 = [&](int j, const uint8_t* k_next, uint8_t* k_fill, const uint8_t* v_prev,
+                     uint8_t* v_fill, f32x16* s_cur, f32x16* s_next, P8Regs& p_cur,
+                     const P8Regs& p_prev) __attribute__((always_inline)) {
+      if (needs_mask(j)) mask(s_cur, j * kBC);
+      if (resc_prev) {  // O^T still holds blocks up to j-2 only
+  #pragma unroll
+        for (int t = 0; t < NDT; ++t) acc[t] *= alpha_prev;
+      }
+      load_v8((j + 2) * kBC, v_fill);   // V(j+2)
+      load_k((j + 3) * kBC, k_fill);    // K(j+3)
+      pv8(v_prev, p_prev);              // P V of block j-1
+      qk(k_next, s_next);               // QK^T of block j+1
+      alpha_prev = softmax8(s_cur, p_cur, resc_prev);
+      mfma_run_pipeline<NDT, 4, NQK, KCH, 2, VPM8, TPM8, 0, NVM8, VM08>();
+      // Keep the whole run -- softmax, P V and QK^T MFMAs -- in this block:
+      // the compiler would otherwise sink MFMAs past the barrier to their
+      // first use in the next iteration.
+  #pragma unroll
+      for (int i = 0; i < 9; ++i) asm volatile("" ::"v"(p_cur[i]));
+      asm volatile("" ::"v"(l_run));
+  #pragma unroll
+      for (int t = 0; t < NDT; ++t)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(acc[t][i]));
+  #pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(s_next[kt][i]));
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVM8) : "memory");
+      barrier();
+    };
+    auto step8_0 = [&](int j) __attribute__((always_inline)) { step8(j, k_lds1, k_lds3, v_lds3, v_lds2, sa, sb, pa, pb); };
+    auto step8_1 = [&](int j) __attribute__((always_inline)) { step8(j, k_lds2, k_lds0, v_lds0, v_lds3, sb, sa, pb, pa); };
+    auto step8_2 = [&](int j) __attribute__((always_inline)) { step8(j, k_lds3, k_lds1, v_lds1, v_lds0, sa, sb, pa, pb); };
+    auto step8_3 = [&](int j) __attribute__((always_inline)) { step8(j, k_lds0, k_lds2, v_lds2, v_lds1, sb, sa, pb, pa); };
+    for (int j = 0; j < nblk; j += 4) {
+      step8_0(j);
+      step8_1(j + 1);
+      step8_2(j + 2);
+      step8_3(j + 3);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS load outlives the loop
-    pv(vbuf, p_last);
-    mfma_read_pipeline<NPV, 1, (NPV < 8 ? NPV : 8)>();
-  };
-  // The loop runs to the next multiple of four blocks: blocks past the last
-  // one are fully masked (keys past N, or causal keys after every query of the
-  // workgroup), so they change neither m, l nor O.  One copy of the loop body
-  // keeps the register allocation of the steady state.
-  for (int j = 0; j < nblk; j += 4) {
-    step0(j);
-    step1(j + 1);
-    step2(j + 2);
-    step3(j + 3);
-  }
-  last_pv(v_lds1, pb);  // the last iteration is odd: P in pb, V^T in buffer 1
+    if (resc_prev) {
+  #pragma unroll
+      for (int t = 0; t < NDT; ++t) acc[t] *= alpha_prev;
+    }
+    pv8(v_lds3, pb);  // the last iteration is j % 4 == 3: P in pb, V in stage 3
+    mfma_read_pipeline<NDT, 4, (NDT < 2 ? NDT : 2)>();
+    }
 
   // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
@@ -669,16 +889,24 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   return FA_OK;
 }
 
-template <int DT, int D, bool CAUSAL, int WAVES>
-int launch_w(Params prm, hipStream_t stream) {
+// Query tiles [qt_lo, qt_hi) of every head (tiles of Shape<WAVES>::br rows).
+template <int DT, int D, bool CAUSAL, int WAVES, bool PV8 = false>
+int launch_w(Params prm, int qt_lo, int qt_hi, hipStream_t stream) {
   using S = Shape<WAVES>;
-  prm.n_qtiles = (prm.N + S::br - 1) / S::br;
+  prm.qt_base = qt_lo;
+  prm.n_qtiles = qt_hi - qt_lo;
   void* args[] = {&prm};
   const dim3 grid((unsigned)(prm.bh * prm.n_qtiles));
   hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, WAVES>), grid,
+      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, WAVES, PV8>), grid,
       dim3(S::threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int DT, int D, bool CAUSAL, int WAVES>
+int launch_all(const Params& prm, hipStream_t stream) {
+  return launch_w<DT, D, CAUSAL, WAVES>(prm, 0, (prm.N + Shape<WAVES>::br - 1) / Shape<WAVES>::br,
+                                        stream);
 }
 
 template <int DT, int D, bool CAUSAL>
@@ -688,9 +916,32 @@ int launch_t(const Params& prm, hipStream_t stream) {
     // With 256-row tiles filling at most half the CUs, 128-row tiles on all of
     // them finish sooner although one wave per SIMD runs slower than two.
     const int64_t wgs = (int64_t)prm.bh * ((prm.N + Shape<8>::br - 1) / Shape<8>::br);
-    if (2 * wgs <= kCUs) return launch_w<DT, D, CAUSAL, 4>(prm, stream);
+    if (2 * wgs <= kCUs) return launch_all<DT, D, CAUSAL, 4>(prm, stream);
   }
-  return launch_w<DT, D, CAUSAL, W>(prm, stream);
+  return launch_all<DT, D, CAUSAL, W>(prm, stream);
+}
+
+// fp8 with P V on the fp8 matrix cores for every query tile whose first row
+// sees at least min_keys keys (causal: row i sees i + 1; otherwise all N), and
+// in fp16 for the tiles before: two launches over disjoint tiles, both with
+// 128-row tiles.
+template <int D, bool CAUSAL>
+int launch_pv8(const Params& prm, int64_t min_keys, hipStream_t stream) {
+  constexpr int DT = FA_DTYPE_FP8_E4M3;
+  constexpr int BR = Shape<4>::br;
+  static_assert(default_waves<DT, D>() == 4, "both launches use 128-row tiles");
+  const int n_t = (prm.N + BR - 1) / BR;
+  const int64_t mk = min_keys < (int64_t)prm.N + 1 ? min_keys : (int64_t)prm.N + 1;
+  int n_lo;  // tiles that keep P V in fp16
+  if (CAUSAL)
+    n_lo = mk <= 1 ? 0 : (int)((mk - 1 + BR - 1) / BR);  // first row qt*BR sees qt*BR + 1 keys
+  else
+    n_lo = prm.N >= mk ? 0 : n_t;
+  if (n_lo > n_t) n_lo = n_t;
+  int st = FA_OK;
+  if (n_lo > 0) st = launch_w<DT, D, CAUSAL, 4, false>(prm, 0, n_lo, stream);
+  if (st == FA_OK && n_lo < n_t) st = launch_w<DT, D, CAUSAL, 4, true>(prm, n_lo, n_t, stream);
+  return st;
 }
 
 template <int DT>
@@ -699,9 +950,12 @@ int launch_dt(const Params& prm, int d, int causal, hipStream_t stream) {
   return causal ? launch_t<DT, 128, true>(prm, stream) : launch_t<DT, 128, false>(prm, stream);
 }
 
+// pv8_min_keys < 0: P V in fp16 throughout; otherwise (fp8 only) the split
+// of launch_pv8.
 int run(const void* q, const void* k, const void* v, const float* dq, const float* dk,
         const float* dv, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
-        float scale, int causal, int dtype, int layout, void* stream) {
+        float scale, int causal, int dtype, int layout, void* stream,
+        int64_t pv8_min_keys = -1) {
   Params prm;
   prm.q = static_cast<const uint8_t*>(q);
   prm.k = static_cast<const uint8_t*>(k);
@@ -716,8 +970,16 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   prm.n_qtiles = 0;  // set per kernel shape at launch
   prm.bh = (int)(B * H);
   prm.layout = layout;
+  prm.qt_base = 0;
   prm.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == FA_DTYPE_FP8_E4M3 && pv8_min_keys >= 0) {
+    if (d == 64)
+      return causal ? launch_pv8<64, true>(prm, pv8_min_keys, s)
+                    : launch_pv8<64, false>(prm, pv8_min_keys, s);
+    return causal ? launch_pv8<128, true>(prm, pv8_min_keys, s)
+                  : launch_pv8<128, false>(prm, pv8_min_keys, s);
+  }
   switch (dtype) {
     case FA_DTYPE_FP16: return launch_dt<FA_DTYPE_FP16>(prm, (int)d, causal, s);
     case FA_DTYPE_BF16: return launch_dt<FA_DTYPE_BF16>(prm, (int)d, causal, s);
@@ -772,6 +1034,24 @@ extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, const floa
              layout, stream);
 }
 
+extern "C" int fa_fwd_fp8_pv(const void* q, const void* k, const void* v, const float* descale_q,
+                             const float* descale_k, const float* descale_v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                             int layout, int64_t min_keys, void* stream) {
+  bool empty;
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, FA_DTYPE_FP8_E4M3, layout,
+                      &empty);
+  if (st != FA_OK) return st;
+  if (min_keys < 0) return FA_ERR_MIN_KEYS;
+  if (empty) return FA_OK;
+  const int given = (descale_q != nullptr) + (descale_k != nullptr) + (descale_v != nullptr);
+  if (given != 0 && given != 3) return FA_ERR_NULL;
+  if (given == 3 && (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
+    return FA_ERR_ALIGN;
+  return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal,
+             FA_DTYPE_FP8_E4M3, layout, stream, min_keys);
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -784,6 +1064,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "scale must be finite and positive";
     case FA_ERR_CAUSAL: return "causal must be 0 or 1";
     case FA_ERR_LAYOUT: return "layout must be FA_LAYOUT_BHND or FA_LAYOUT_BNHD";
+    case FA_ERR_MIN_KEYS: return "min_keys must be >= 0";
     default: return "unknown status";
   }
 }

@@ -45,6 +45,10 @@ def parse_args(argv=None):
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="time the forward pass (default) or the backward pass (fa_bwd, "
                          "fp16/bf16 workloads; counted FLOPs 10*B*H*N^2*d, halved if causal)")
+    ap.add_argument("--fp8-pv", type=int, default=None, metavar="MIN_KEYS",
+                    help="fp8 workloads: P V on the fp8 matrix instructions as well "
+                         "(fa_fwd_fp8_pv) for query tiles whose first row sees at least "
+                         "MIN_KEYS keys (512 keeps the fp8 error bars)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -120,7 +124,7 @@ class ClockSampler:
         return sum(s) / len(s) if s else None
 
 
-def time_gpu(inp, steps, warmup, clock=None, layout="bhnd"):
+def time_gpu(inp, steps, warmup, clock=None, layout="bhnd", pv8=None):
     """Average seconds per fa_fwd call, HIP events on the launch stream; with a
     ClockSampler, afterwards the mean graphics clock under the same load."""
     import torch
@@ -137,7 +141,10 @@ def time_gpu(inp, steps, warmup, clock=None, layout="bhnd"):
     out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
 
     def step():
-        if layout == "bnhd":
+        if pv8 is not None and inp.dtype == "fp8":
+            binding.fwd_fp8_pv(q, k, v, min_keys=pv8, layout=layout, causal=inp.causal,
+                               scale=inp.scale, descales=ds, out=out, lse=lse)
+        elif layout == "bnhd":
             binding.fwd_ex(q, k, v, layout="bnhd", causal=inp.causal, scale=inp.scale,
                            descales=ds, out=out, lse=lse)
         elif inp.dtype == "fp8":
@@ -288,14 +295,17 @@ def main(argv=None):
             "frac_of_peak": round(tf / peak, 4)}), flush=True)
         return 0
     clock = ClockSampler()
-    sec = time_gpu(inp, args.steps, args.warmup, clock, args.layout)
+    sec = time_gpu(inp, args.steps, args.warmup, clock, args.layout, args.fp8_pv)
     flops, tf, peak = describe(inp, sec)
     if args.sweep:
         for cfg in inputs.CONFIGS + inputs.EXTRA_WORKLOADS:
             x = inputs.draw(*cfg[1:8])
-            s = time_gpu(x, max(10, args.steps // 4), args.warmup, None, args.layout)
+            s = time_gpu(x, max(10, args.steps // 4), args.warmup, None, args.layout,
+                         args.fp8_pv)
             _, t, pk = describe(x, s)
-            print(json.dumps({"workload": cfg[0], "layout": args.layout, "ms": round(s * 1e3, 4),
+            print(json.dumps({"workload": cfg[0], "layout": args.layout,
+                              "fp8_pv": args.fp8_pv if x.dtype == "fp8" else None,
+                              "ms": round(s * 1e3, 4),
                               "tflops": round(t, 2), "frac": round(t / pk, 4)}),
                   file=sys.stderr, flush=True)
     rec = {
@@ -313,7 +323,9 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": name, "layout": args.layout, "B": B, "H": H, "N": N, "d": d,
                    "input_dtype": dtype, "causal": bool(causal), "seed": seed,
-                   "outputs": "O fp16 + LSE fp32", "accumulate": "fp32"},
+                   "outputs": "O fp16 + LSE fp32", "accumulate": "fp32",
+                   **({"pv": f"fp8 from min_keys={args.fp8_pv}"}
+                      if args.fp8_pv is not None and dtype == "fp8" else {})},
         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tf / peak, 4),
                      "traffic": measured_traffic(name, args.layout)},

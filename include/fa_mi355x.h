@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
   FA_DTYPE_FP16 = 0,      /* IEEE binary16 */
@@ -67,7 +67,8 @@ typedef enum {
   FA_ERR_LAUNCH = -6,     /* the HIP runtime refused the kernel launch */
   FA_ERR_SCALE = -7,      /* scale not finite and positive */
   FA_ERR_CAUSAL = -8,     /* causal not 0 or 1 */
-  FA_ERR_LAYOUT = -9      /* unknown tensor layout */
+  FA_ERR_LAYOUT = -9,     /* unknown tensor layout */
+  FA_ERR_MIN_KEYS = -10   /* fa_fwd_fp8_pv: min_keys negative */
 } fa_status;
 
 /* Memory layout of q, k, v and o (lse is always [B, H, N]). */
@@ -123,6 +124,31 @@ int fa_fwd_ex(const void* q, const void* k, const void* v,
               int causal, int dtype, int layout, void* stream);
 
 /*
+ * fa_fwd_fp8_pv -- fa_fwd_ex for fp8 inputs with P V on the fp8 matrix
+ * instructions as well, the fp8 scheme of "第 17 章 TMA + Warp Specialization
+ * 把 FA2 写到 SOTA" (section 17.7: softmax output converted to fp8 before
+ * the P V product, scales per block).  Here each query row's probabilities
+ * of one 64-key block are multiplied by a power of two 2^k that brings the
+ * largest into (128, 256], rounded to e4m3 (round to nearest even), and the
+ * matrix instruction scales them back by 2^-k; the row sum is taken before
+ * the rounding.  e4m3 keeps 3 fraction bits, so a row that sees few keys
+ * loses accuracy: query tiles (128 rows) whose first row sees fewer than
+ * min_keys keys (causal: row i sees i + 1; otherwise every row sees N) run
+ * P V in fp16 exactly as fa_fwd_ex does.  min_keys = 0 puts every tile on
+ * fp8 P V; min_keys > N gives fa_fwd_ex's result bit for bit.  512 keeps
+ * max |O error| within 3e-2 on N(0, 1) inputs quantized per head (measured
+ * 1.2e-2 at rows 512-1023, below 4e-3 past row 4096).  Other arguments as for
+ * fa_fwd_ex with dtype FA_DTYPE_FP8_E4M3 (descales: all three or none);
+ * min_keys < 0 returns FA_ERR_MIN_KEYS.  One or two kernels are enqueued
+ * (disjoint query tiles).  Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd_fp8_pv(const void* q, const void* k, const void* v,
+                  const float* descale_q, const float* descale_k,
+                  const float* descale_v, void* o, float* lse,
+                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                  int causal, int layout, int64_t min_keys, void* stream);
+
+/*
  * fa_bwd -- gradients of the attention forward pass (fp16 or bf16 inputs,
  * [B, H, N, d] layout).  Given dout = dL/dO for some loss L, it writes
  *
@@ -139,8 +165,8 @@ int fa_fwd_ex(const void* q, const void* k, const void* v,
  * same q, k, v, scale and causal (fa_fwd's, or any consistent pair).  All
  * pointers are device pointers, 16-byte aligned, none NULL when B*H*N > 0;
  * the library allocates nothing (delta is the caller's workspace and an
- * output).  dtype FP8 returns FA_ERR_DTYPE.  Two kernels are enqueued on the
- * stream.  Returns FA_OK or a negative fa_status.
+ * output).  dtype FP8 returns FA_ERR_DTYPE.  Three kernels are enqueued on
+ * the stream (dQ with delta, then dV, then dK).  Returns FA_OK or a negative fa_status.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, float* dq, float* dk, float* dv,

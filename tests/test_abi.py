@@ -201,3 +201,37 @@ def test_fa_bwd_rejects(kw, status):
 def test_fa_bwd_empty_is_a_noop():
     assert _call_bwd(N=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None,
                      dv=None, delta=None) == 0
+
+
+def _call_pv(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, dq=None, dk=None, dv=None, o=O, lse=L, B=1, H=2, N=256, d=128,
+                scale=0.1, causal=1, layout=0, min_keys=512, stream=None)
+    args.update(kw)
+    return lib.fa_fwd_fp8_pv(args["q"], args["k"], args["v"], args["dq"], args["dk"],
+                             args["dv"], args["o"], args["lse"], args["B"], args["H"],
+                             args["N"], args["d"], args["scale"], args["causal"],
+                             args["layout"], args["min_keys"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(min_keys=-1), "FA_ERR_MIN_KEYS"),
+    (dict(min_keys=-(1 << 40), N=0), "FA_ERR_MIN_KEYS"),
+    (dict(layout=3), "FA_ERR_LAYOUT"),
+    (dict(d=256), "FA_ERR_HEAD_DIM"),
+    (dict(causal=2), "FA_ERR_CAUSAL"),
+    (dict(scale=float("inf")), "FA_ERR_SCALE"),
+    (dict(v=None), "FA_ERR_NULL"),
+    (dict(lse=L + 2), "FA_ERR_ALIGN"),
+    (dict(dq=A + 0x5000), "FA_ERR_NULL"),
+    (dict(dq=A + 0x5000, dk=A + 0x6000, dv=A + 0x7001), "FA_ERR_ALIGN"),
+    (dict(N=1 << 20, H=1 << 4, d=128, layout=1), "FA_ERR_SHAPE"),
+])
+def test_fa_fwd_fp8_pv_rejects(kw, status):
+    assert _call_pv(**kw) == _header_constants()[status]
+
+
+@pytest.mark.parametrize("min_keys", [0, 512, 1 << 62])
+def test_fa_fwd_fp8_pv_empty_is_a_noop(min_keys):
+    assert _call_pv(min_keys=min_keys, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert _call_pv(min_keys=min_keys, H=0) == 0
