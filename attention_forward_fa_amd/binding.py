@@ -37,6 +37,11 @@ SIGNATURES = {
                                  ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]),
     "fa_fwd_fp8_pv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                      ctypes.c_float, ctypes.c_int, ctypes.c_int, _I64, _P]),
+    "fa_fwd_kvsplit_workspace": (ctypes.c_int64, [_I64, _I64, _I64, _I64, ctypes.c_int,
+                                                   ctypes.c_int]),
+    "fa_fwd_kvsplit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                                      ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      _P, _I64, _P]),
     "fa_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                               ctypes.c_float, ctypes.c_int, ctypes.c_int, _P]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -237,6 +242,43 @@ def fwd_fp8_pv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, min_keys: int 
         st = lib.fa_fwd_fp8_pv(_ptr(q), _ptr(k), _ptr(v), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(out), _ptr(lse), B, H, N, d, scale, int(bool(causal)),
                                LAYOUTS[layout], int(min_keys), stream)
+    _check(st)
+    return out, lse
+
+
+def kvsplit_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool, dtype) -> int:
+    """fa_fwd_kvsplit_workspace: device bytes fwd_kvsplit needs (0: it will not split)."""
+    code = _TORCH_DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    n = load_library().fa_fwd_kvsplit_workspace(B, H, N, d, int(bool(causal)), code)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bhnd",
+                causal: bool = False, scale: Optional[float] = None,
+                descales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fa_fwd_kvsplit: fwd_ex with long query tiles' key ranges split over several
+    workgroups and merged.  workspace: a device tensor of at least
+    kvsplit_workspace_bytes(...) bytes (allocated here when not given)."""
+    B, H, N, d = _layout_shape(q, layout)
+    _validate(q, k, v)
+    dq, dk, dv = _descale_ptrs(q, descales, B, H)
+    out, lse = _outputs(q, out, lse, layout)
+    scale = _default_scale(d) if scale is None else float(scale)
+    need = kvsplit_workspace_bytes(B, H, N, d, causal, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_fwd_kvsplit(_ptr(q), _ptr(k), _ptr(v), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(out), _ptr(lse), B, H, N, d, scale, int(bool(causal)),
+                                _TORCH_DTYPE_CODE[q.dtype], LAYOUTS[layout], _ptr(workspace),
+                                ws_bytes, stream)
     _check(st)
     return out, lse
 

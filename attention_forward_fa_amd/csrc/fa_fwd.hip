@@ -205,6 +205,17 @@ struct Params {
   int layout;  // FA_LAYOUT_BHND or FA_LAYOUT_BNHD (q, k, v and o alike)
   int qt_base; // first query tile of this launch (n_qtiles tiles from there)
   float scale;
+  // Key-range split (split_g > 0): workgroup w takes head w % bh and the
+  // (w / bh)-th chunk of that head, longest tiles first.  A tile's key range,
+  // in groups of BR/64 blocks (causal tile t: t + 1 groups; otherwise
+  // ceil(N / BR)), is cut into ceil(groups / split_g) chunks of near-equal
+  // size.  Tiles with one chunk write O and LSE; the others write their
+  // chunk's O (fp32, normalised) and LSE to ws_o / ws_lse, slot
+  // ((bh * n_qtiles + t) * split_cmax + chunk) * BR + row, for the merge.
+  int split_g;
+  int split_cmax;
+  float* ws_o;
+  float* ws_lse;
 };
 
 
@@ -275,8 +286,32 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
 
   // ---- work decomposition: one workgroup per (b*H + h, query tile) ----------
   int bh, qt;
-  tile_of(blockIdx.x, p.bh, p.n_qtiles, CAUSAL, bh, qt);
-  qt += p.qt_base;
+  // Key blocks [kb_lo, kb_hi) of the tile's range; n_chunks > 1 when the
+  // range is split over several workgroups.
+  int kb_lo = 0, kb_hi = 0, chunk = 0, n_chunks = 1, n_groups = 0;
+  if (p.split_g > 0) {
+    bh = blockIdx.x % p.bh;
+    int u = blockIdx.x / p.bh;
+    const int g = p.split_g;
+    if (CAUSAL) {
+      qt = p.n_qtiles - 1;
+      while (u >= (qt + g) / g) {  // tile qt: ceil((qt + 1) / g) chunks
+        u -= (qt + g) / g;
+        --qt;
+      }
+      n_groups = qt + 1;
+    } else {
+      n_groups = (p.N + kBR - 1) / kBR;
+      const int per_tile = (n_groups + g - 1) / g;
+      qt = u / per_tile;
+      u -= qt * per_tile;
+    }
+    chunk = u;
+    n_chunks = (n_groups + g - 1) / g;
+  } else {
+    tile_of(blockIdx.x, p.bh, p.n_qtiles, CAUSAL, bh, qt);
+    qt += p.qt_base;
+  }
   const int N = p.N;
   // Element offset of the head's first row and the stride between its rows:
   // [B, H, N, d] (rows of one head adjacent) or [B, N, H, d] (rows of one head
@@ -328,7 +363,16 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   // ---- K/V blocks this workgroup visits --------------------------------------
   int kv_end = N;
   if constexpr (CAUSAL) kv_end = min(N, q0 + kBR);
-  const int nblk = (kv_end + kBC - 1) / kBC;
+  kb_hi = (kv_end + kBC - 1) / kBC;
+  if (n_chunks > 1) {
+    // Chunk boundaries fall on whole groups, so the first block of a chunk
+    // starts at or before the tile's first row (causal) and below N: every
+    // row of the tile has a key in it, as the running max requires.
+    constexpr int A = kBR / kBC;  // blocks per group
+    kb_lo = A * (chunk * n_groups / n_chunks);
+    kb_hi = min(kb_hi, A * ((chunk + 1) * n_groups / n_chunks));
+    kv_end = min(kv_end, kb_hi * kBC);
+  }
 
   // ---- staging -----------------------------------------------------------------
   // All eight waves stage.  K goes global -> LDS directly (buffer_load ...
@@ -510,7 +554,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   // with every key masked for this lane leaves m_run, l_run unchanged and
   // contributes P = 0 (block 0 always holds a valid key for every row).
   auto needs_mask = [&](int j) __attribute__((always_inline)) {
-    return (j * kBC + kBC > N) || (CAUSAL && j * kBC + kBC - 1 > qw0);
+    return (j * kBC + kBC > kv_end) || (CAUSAL && j * kBC + kBC - 1 > qw0);
   };
   auto mask = [&](f32x16* st, int kb) __attribute__((always_inline)) {
 #pragma unroll
@@ -518,7 +562,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb + kt * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-        bool keep = key < N;
+        bool keep = key < kv_end;
         if constexpr (CAUSAL) keep = keep && key <= my_q;
         st[kt][i] = keep ? st[kt][i] : -INFINITY;
       }
@@ -681,10 +725,10 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
       reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0u, 0u, 0u, 0u};
     }
     constexpr int NVM = K_PER_W + 4;  // global load instructions per wave per iteration
-    load_k(0, k_lds0);
-    load_k(kBC, k_lds1);
-    load_v(0, vst);
-    load_k(2 * kBC, k_lds2);
+    load_k(kb_lo * kBC, k_lds0);
+    load_k((kb_lo + 1) * kBC, k_lds1);
+    load_v(kb_lo * kBC, vst);
+    load_k((kb_lo + 2) * kBC, k_lds2);
     // This wave's K(0) and K(1) have landed; V(0) and K(2) may still fly.
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 + K_PER_W) : "memory");
     barrier();
@@ -743,7 +787,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     // one are fully masked (keys past N, or causal keys after every query of the
     // workgroup), so they change neither m, l nor O.  One copy of the loop body
     // keeps the register allocation of the steady state.
-    for (int j = 0; j < nblk; j += 4) {
+    for (int j = kb_lo; j < kb_hi; j += 4) {
       step0(j);
       step1(j + 1);
       step2(j + 2);
@@ -759,11 +803,11 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     for (int i = tid; i < KBUF / 16; i += kThreads)
       reinterpret_cast<u32x4*>(v_lds3)[i] = u32x4{0u, 0u, 0u, 0u};
     constexpr int NVM8 = 2 * K_PER_W;  // global load instructions per wave per iteration
-    load_k(0, k_lds0);
-    load_v8(0, v_lds0);
-    load_k(kBC, k_lds1);
-    load_v8(kBC, v_lds1);
-    load_k(2 * kBC, k_lds2);
+    load_k(kb_lo * kBC, k_lds0);
+    load_v8(kb_lo * kBC, v_lds0);
+    load_k((kb_lo + 1) * kBC, k_lds1);
+    load_v8((kb_lo + 1) * kBC, v_lds1);
+    load_k((kb_lo + 2) * kBC, k_lds2);
     // This wave's K(0), V(0) and K(1) have landed; V(1) and K(2) may still fly.
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVM8) : "memory");
     barrier();
@@ -819,7 +863,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     auto step8_1 = [&](int j) __attribute__((always_inline)) { step8(j, k_lds2, k_lds0, v_lds0, v_lds3, sb, sa, pb, pa); };
     auto step8_2 = [&](int j) __attribute__((always_inline)) { step8(j, k_lds3, k_lds1, v_lds1, v_lds0, sa, sb, pa, pb); };
     auto step8_3 = [&](int j) __attribute__((always_inline)) { step8(j, k_lds0, k_lds2, v_lds2, v_lds1, sb, sa, pb, pa); };
-    for (int j = 0; j < nblk; j += 4) {
+    for (int j = kb_lo; j < kb_hi; j += 4) {
       step8_0(j);
       step8_1(j + 1);
       step8_2(j + 2);
@@ -836,7 +880,24 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
 
   // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
-  if (my_q < N) {
+  if (my_q < N && n_chunks > 1) {
+    // One chunk of a split key range: O over the chunk's keys (fp32) and its
+    // LSE, for the merge.
+    const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;
+    const int64_t slot =
+        ((int64_t)(bh * p.n_qtiles + qt) * p.split_cmax + chunk) * kBR + (my_q - q0);
+    float* orow = p.ws_o + slot * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = t * 32 + 8 * g + 4 * hh;
+        *reinterpret_cast<f32x4*>(orow + d0) =
+            f32x4{acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv, acc[t][4 * g + 2] * inv,
+                  acc[t][4 * g + 3] * inv};
+      }
+    if (hh == 0) p.ws_lse[slot] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
+  } else if (my_q < N) {
     const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;
     _Float16* orow = p.o + head_off + (int64_t)my_q * row_elems;
 #pragma unroll
@@ -853,14 +914,78 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
 }
 
 // ---------------------------------------------------------------------------
+// Merge of split key ranges: for each row of a tile whose range was cut into
+// chunks, LSE = ln sum_c exp(LSE_c) and O = sum_c exp(LSE_c - LSE) O_c (softmax
+// over a union of key sets from the softmaxes over the parts), O rounded to
+// fp16.
+// ---------------------------------------------------------------------------
+struct MergeParams {
+  const float* ws_o;
+  const float* ws_lse;
+  _Float16* o;
+  float* lse;
+  int N;
+  int H;
+  int n_qtiles;
+  int layout;
+  int split_g;
+  int split_cmax;
+  int causal;
+};
+
+template <int D, int BR>
+__global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
+  // One thread per row and 4 d values, so every load of a row's chunks is
+  // independent and many are in flight: the merge is a pass over the partials
+  // at memory speed.
+  constexpr int TPR = D / 4;          // threads per row
+  constexpr int RPW = 256 / TPR;      // rows per workgroup
+  constexpr int WPT = BR / RPW;       // workgroups per tile
+  const int tile = blockIdx.x / WPT;  // bh * n_qtiles + qt
+  const int bh = tile / m.n_qtiles, qt = tile % m.n_qtiles;
+  const int groups = m.causal ? qt + 1 : m.n_qtiles;
+  const int n = (groups + m.split_g - 1) / m.split_g;
+  if (n < 2) return;  // written by the attention kernel itself
+  const int r = (blockIdx.x % WPT) * RPW + threadIdx.x / TPR;
+  const int row = qt * BR + r;
+  if (row >= m.N) return;
+  const int e0 = (threadIdx.x % TPR) * 4;
+  const int64_t slot0 = (int64_t)tile * m.split_cmax * BR + r;  // chunk c: slot0 + c * BR
+  float mx = -INFINITY;
+  for (int ch = 0; ch < n; ++ch) mx = fmaxf(mx, m.ws_lse[slot0 + (int64_t)ch * BR]);
+  float wsum = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int ch = 0; ch < n; ++ch) {
+    const int64_t slot = slot0 + (int64_t)ch * BR;
+    const float w = __expf(m.ws_lse[slot] - mx);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(m.ws_o + slot * D + e0);
+    wsum += w;
+    acc += w * x;
+  }
+  const float inv = 1.0f / wsum;
+  int64_t off;
+  if (m.layout == FA_LAYOUT_BNHD) {
+    const int b = bh / m.H, h = bh - b * m.H;
+    off = (((int64_t)b * m.N + row) * m.H + h) * D;
+  } else {
+    off = ((int64_t)bh * m.N + row) * D;
+  }
+  _Float16* dst = m.o + off + e0;
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_f16x2(acc[0] * inv, acc[1] * inv),
+                                         pack_f16x2(acc[2] * inv, acc[3] * inv)};
+  if (e0 == 0) m.lse[(int64_t)bh * m.N + row] = mx + __logf(wsum);
+}
+
+// ---------------------------------------------------------------------------
 // Host side: argument checks (no HIP calls) and launch.
 // ---------------------------------------------------------------------------
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
-               int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
-               int layout, bool* empty) {
+// Everything but the pointers.
+int check_problem(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
+                  int layout, bool* empty) {
   *empty = false;
   if (layout != FA_LAYOUT_BHND && layout != FA_LAYOUT_BNHD) return FA_ERR_LAYOUT;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
@@ -882,6 +1007,14 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   if (layout == FA_LAYOUT_BNHD && N * H * d * esize > (int64_t)1 << 30) return FA_ERR_SHAPE;
   const int64_t tiles = (N + kMinBR - 1) / kMinBR;
   if (B * H * tiles > INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
+               int layout, bool* empty) {
+  const int st = check_problem(B, H, N, d, scale, causal, dtype, layout, empty);
+  if (st != FA_OK || *empty) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4))
@@ -950,12 +1083,133 @@ int launch_dt(const Params& prm, int d, int causal, hipStream_t stream) {
   return causal ? launch_t<DT, 128, true>(prm, stream) : launch_t<DT, 128, false>(prm, stream);
 }
 
+// Key-range split for grids that would leave CUs idle or hand the causal tail
+// to a few of them.  Work is counted in groups (BR x BR score blocks, BR the
+// kernel's tile height): with T tiles per head, causal tile t spans t + 1
+// groups and a non-causal one T.  Cutting each tile into ceil(groups / g)
+// chunks of at most g groups gives `units` workgroups; with `slots`
+// workgroups resident at once (one per CU for 8-wave kernels, two for 4-wave)
+// the attention kernel takes about ceil(units / slots) rounds of g + 1/2
+// group times (the half for a chunk's prologue and epilogue), and every chunk
+// of a split tile adds its partial O and LSE, written and read back once, at
+// an effective 5 TB/s.  A group takes 4 BR^2 d FLOP at the slot's share of
+// the kernel's measured throughput (about 1.0 PFLOP/s for fp16 / bf16, 1.3
+// for fp8, 0.6 of that at d = 64).  Unsplit, the time is the longest tile or
+// the work per slot, whichever is larger -- for an 8-wave grid small enough
+// to run on the 4-wave twin, with the twin's 128-row tiles (half a group row
+// each) at about 0.8 of the 8-wave rate.  The split is taken when estimated
+// at least 20 % faster; grids with at least two tiles per slot are left whole
+// (the longest-first order balances them).
+struct SplitPlan {
+  int g = 0;     // chunk size in groups; 0: no split
+  int cmax = 0;  // chunks of the longest tile
+  int T = 0;     // query tiles per head
+  int br = 0;    // rows per tile
+  int64_t units = 0;
+  int64_t ws_bytes = 0;
+};
+
+SplitPlan plan_split(int64_t BH, int64_t N, int64_t d, bool causal, int dtype) {
+  SplitPlan pl;
+  const int br = (d == 128 && dtype != FA_DTYPE_FP8_E4M3) ? 256 : 128;  // default_waves * 32
+  const int64_t slots = (int64_t)kCUs * (br == 256 ? 1 : 2);
+  const int64_t T = (N + br - 1) / br;
+  pl.T = (int)T;
+  pl.br = br;
+  if (T < 4 || BH * T >= 2 * slots) return pl;
+  auto chunks_per_head = [&](int64_t g) {
+    if (!causal) return T * ((T + g - 1) / g);
+    const int64_t full = T / g, rem = T % g;  // sum over t < T of ceil((t + 1) / g)
+    return g * full * (full + 1) / 2 + rem * (full + 1);
+  };
+  const double rate = (dtype == FA_DTYPE_FP8_E4M3 ? 1.3e15 : 1.0e15) * (d == 64 ? 0.6 : 1.0);
+  const double t_group = 4.0 * br * br * (double)d / (rate / (double)slots);  // seconds
+  const double t_partial = 2.0 * br * (d + 1) * 4.0 / 5e12;                  // seconds per chunk
+  const int64_t total = causal ? BH * T * (T + 1) / 2 : BH * T * T;
+  double whole;
+  if (br == 256 && 2 * BH * T <= kCUs) {  // launch_t runs the 4-wave twin
+    const double longest = 0.5 * (double)T / 0.8;
+    whole = t_group * (causal ? fmax(longest, (double)total / (0.8 * kCUs)) : longest);
+  } else {
+    whole = t_group * (causal ? fmax((double)T, (double)((total + slots - 1) / slots))
+                              : (double)((BH * T + slots - 1) / slots) * (double)T);
+  }
+  double best = whole;
+  for (int64_t g = T - 1; g >= 1; --g) {  // ties go to fewer, longer chunks
+    const int64_t per_head = chunks_per_head(g);
+    const int64_t units = BH * per_head;
+    // chunks of split tiles: all but the tiles short enough for one chunk
+    const int64_t whole_tiles = causal ? (g < T ? g : T) : (g >= T ? T : 0);
+    const int64_t split_chunks = BH * (per_head - whole_tiles);
+    const double est = (double)((units + slots - 1) / slots) * ((double)g + 0.5) * t_group +
+                       (double)split_chunks * t_partial;
+    if (est < best) {
+      best = est;
+      pl.g = (int)g;
+    }
+  }
+  if (pl.g == 0 || best > 0.8 * whole) {
+    pl.g = 0;
+    return pl;
+  }
+  pl.cmax = (int)((T + pl.g - 1) / pl.g);
+  pl.units = BH * chunks_per_head(pl.g);
+  pl.ws_bytes = BH * T * pl.cmax * br * (d + 1) * (int64_t)sizeof(float);
+  return pl;
+}
+
+template <int DT, int D, bool CAUSAL>
+int launch_split(Params prm, const SplitPlan& pl, void* ws, hipStream_t stream) {
+  constexpr int W = default_waves<DT, D>();
+  using S = Shape<W>;
+  prm.n_qtiles = pl.T;
+  prm.qt_base = 0;
+  prm.split_g = pl.g;
+  prm.split_cmax = pl.cmax;
+  prm.ws_o = static_cast<float*>(ws);
+  prm.ws_lse = prm.ws_o + (int64_t)prm.bh * pl.T * pl.cmax * S::br * D;
+  void* args[] = {&prm};
+  hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, W, false>),
+      dim3((unsigned)pl.units), dim3(S::threads), args, 0, stream);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  MergeParams m;
+  m.ws_o = prm.ws_o;
+  m.ws_lse = prm.ws_lse;
+  m.o = prm.o;
+  m.lse = prm.lse;
+  m.N = prm.N;
+  m.H = prm.H;
+  m.n_qtiles = pl.T;
+  m.layout = prm.layout;
+  m.split_g = pl.g;
+  m.split_cmax = pl.cmax;
+  m.causal = CAUSAL ? 1 : 0;
+  void* margs[] = {&m};
+  constexpr int kMergeWgsPerTile = S::br / (256 / (D / 4));
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_merge_kernel<D, S::br>),
+                      dim3((unsigned)(prm.bh * pl.T * kMergeWgsPerTile)), dim3(256), margs, 0,
+                      stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int DT>
+int launch_split_dt(const Params& prm, int d, int causal, const SplitPlan& pl, void* ws,
+                    hipStream_t s) {
+  if (d == 64)
+    return causal ? launch_split<DT, 64, true>(prm, pl, ws, s)
+                  : launch_split<DT, 64, false>(prm, pl, ws, s);
+  return causal ? launch_split<DT, 128, true>(prm, pl, ws, s)
+                : launch_split<DT, 128, false>(prm, pl, ws, s);
+}
+
 // pv8_min_keys < 0: P V in fp16 throughout; otherwise (fp8 only) the split
-// of launch_pv8.
+// of launch_pv8.  split: a plan with g > 0 runs the key-range split with
+// workspace ws.
 int run(const void* q, const void* k, const void* v, const float* dq, const float* dk,
         const float* dv, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
         float scale, int causal, int dtype, int layout, void* stream,
-        int64_t pv8_min_keys = -1) {
+        int64_t pv8_min_keys = -1, const SplitPlan* split = nullptr, void* ws = nullptr) {
   Params prm;
   prm.q = static_cast<const uint8_t*>(q);
   prm.k = static_cast<const uint8_t*>(k);
@@ -972,7 +1226,18 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   prm.layout = layout;
   prm.qt_base = 0;
   prm.scale = scale;
+  prm.split_g = 0;
+  prm.split_cmax = 0;
+  prm.ws_o = nullptr;
+  prm.ws_lse = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (split && split->g > 0) {
+    switch (dtype) {
+      case FA_DTYPE_FP16: return launch_split_dt<FA_DTYPE_FP16>(prm, (int)d, causal, *split, ws, s);
+      case FA_DTYPE_BF16: return launch_split_dt<FA_DTYPE_BF16>(prm, (int)d, causal, *split, ws, s);
+      default: return launch_split_dt<FA_DTYPE_FP8_E4M3>(prm, (int)d, causal, *split, ws, s);
+    }
+  }
   if (dtype == FA_DTYPE_FP8_E4M3 && pv8_min_keys >= 0) {
     if (d == 64)
       return causal ? launch_pv8<64, true>(prm, pv8_min_keys, s)
@@ -1052,6 +1317,44 @@ extern "C" int fa_fwd_fp8_pv(const void* q, const void* k, const void* v, const 
              FA_DTYPE_FP8_E4M3, layout, stream, min_keys);
 }
 
+extern "C" int64_t fa_fwd_kvsplit_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
+                                            int causal, int dtype) {
+  bool empty;
+  const int st = check_problem(B, H, N, d, 1.0f, causal, dtype, FA_LAYOUT_BHND, &empty);
+  if (st != FA_OK) return st;
+  if (empty) return 0;
+  return plan_split(B * H, N, d, causal != 0, dtype).ws_bytes;
+}
+
+extern "C" int fa_fwd_kvsplit(const void* q, const void* k, const void* v, const float* descale_q,
+                              const float* descale_k, const float* descale_v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                              int dtype, int layout, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  bool empty;
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, layout, &empty);
+  if (st != FA_OK) return st;
+  if (workspace_bytes < 0) return FA_ERR_WORKSPACE;
+  if (empty) return FA_OK;
+  if (dtype == FA_DTYPE_FP8_E4M3) {
+    const int given = (descale_q != nullptr) + (descale_k != nullptr) + (descale_v != nullptr);
+    if (given != 0 && given != 3) return FA_ERR_NULL;
+    if (given == 3 &&
+        (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
+      return FA_ERR_ALIGN;
+  } else {
+    descale_q = descale_k = descale_v = nullptr;
+  }
+  const SplitPlan pl = plan_split(B * H, N, d, causal != 0, dtype);
+  if (pl.g > 0) {
+    if (!workspace) return FA_ERR_NULL;
+    if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
+    if (workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
+  }
+  return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal, dtype,
+             layout, stream, -1, &pl, workspace);
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -1065,6 +1368,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_CAUSAL: return "causal must be 0 or 1";
     case FA_ERR_LAYOUT: return "layout must be FA_LAYOUT_BHND or FA_LAYOUT_BNHD";
     case FA_ERR_MIN_KEYS: return "min_keys must be >= 0";
+    case FA_ERR_WORKSPACE: return "workspace smaller than fa_fwd_kvsplit_workspace requires";
     default: return "unknown status";
   }
 }

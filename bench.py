@@ -37,8 +37,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="workload name (attention_forward_fa_amd.inputs.CONFIGS or "
-                         "EXTRA_WORKLOADS)")
+                    help="workload name (attention_forward_fa_amd.inputs.CONFIGS, "
+                         "EXTRA_WORKLOADS or SHARD_WORKLOADS)")
     ap.add_argument("--layout", default="bhnd", choices=["bhnd", "bnhd"],
                     help="tensor layout of q, k, v, o: [B,H,N,d] (fa_fwd) or [B,N,H,d] "
                          "(fa_fwd_ex)")
@@ -49,6 +49,9 @@ def parse_args(argv=None):
                     help="fp8 workloads: P V on the fp8 matrix instructions as well "
                          "(fa_fwd_fp8_pv) for query tiles whose first row sees at least "
                          "MIN_KEYS keys (512 keeps the fp8 error bars)")
+    ap.add_argument("--kvsplit", action="store_true",
+                    help="run fa_fwd_kvsplit (key ranges of long query tiles split over "
+                         "workgroups and merged; workspace allocated before timing)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -124,7 +127,7 @@ class ClockSampler:
         return sum(s) / len(s) if s else None
 
 
-def time_gpu(inp, steps, warmup, clock=None, layout="bhnd", pv8=None):
+def time_gpu(inp, steps, warmup, clock=None, layout="bhnd", pv8=None, kvsplit=False):
     """Average seconds per fa_fwd call, HIP events on the launch stream; with a
     ClockSampler, afterwards the mean graphics clock under the same load."""
     import torch
@@ -139,9 +142,16 @@ def time_gpu(inp, steps, warmup, clock=None, layout="bhnd", pv8=None):
             return raw.permute(0, 2, 1, 3).contiguous().view(t.dtype)
         q, k, v = bnhd(q), bnhd(k), bnhd(v)
     out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+    ws = None
+    if kvsplit:
+        need = binding.kvsplit_workspace_bytes(inp.B, inp.H, inp.N, inp.d, inp.causal, q.dtype)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step():
-        if pv8 is not None and inp.dtype == "fp8":
+        if kvsplit:
+            binding.fwd_kvsplit(q, k, v, layout=layout, causal=inp.causal, scale=inp.scale,
+                                descales=ds, out=out, lse=lse, workspace=ws)
+        elif pv8 is not None and inp.dtype == "fp8":
             binding.fwd_fp8_pv(q, k, v, min_keys=pv8, layout=layout, causal=inp.causal,
                                scale=inp.scale, descales=ds, out=out, lse=lse)
         elif layout == "bnhd":
@@ -295,16 +305,17 @@ def main(argv=None):
             "frac_of_peak": round(tf / peak, 4)}), flush=True)
         return 0
     clock = ClockSampler()
-    sec = time_gpu(inp, args.steps, args.warmup, clock, args.layout, args.fp8_pv)
+    sec = time_gpu(inp, args.steps, args.warmup, clock, args.layout, args.fp8_pv, args.kvsplit)
     flops, tf, peak = describe(inp, sec)
     if args.sweep:
-        for cfg in inputs.CONFIGS + inputs.EXTRA_WORKLOADS:
+        for cfg in inputs.CONFIGS + inputs.EXTRA_WORKLOADS + inputs.SHARD_WORKLOADS:
             x = inputs.draw(*cfg[1:8])
             s = time_gpu(x, max(10, args.steps // 4), args.warmup, None, args.layout,
-                         args.fp8_pv)
+                         args.fp8_pv, args.kvsplit)
             _, t, pk = describe(x, s)
             print(json.dumps({"workload": cfg[0], "layout": args.layout,
                               "fp8_pv": args.fp8_pv if x.dtype == "fp8" else None,
+                              "kvsplit": args.kvsplit,
                               "ms": round(s * 1e3, 4),
                               "tflops": round(t, 2), "frac": round(t / pk, 4)}),
                   file=sys.stderr, flush=True)
@@ -325,7 +336,8 @@ def main(argv=None):
                    "input_dtype": dtype, "causal": bool(causal), "seed": seed,
                    "outputs": "O fp16 + LSE fp32", "accumulate": "fp32",
                    **({"pv": f"fp8 from min_keys={args.fp8_pv}"}
-                      if args.fp8_pv is not None and dtype == "fp8" else {})},
+                      if args.fp8_pv is not None and dtype == "fp8" else {}),
+                   **({"kvsplit": True} if args.kvsplit else {})},
         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tf / peak, 4),
                      "traffic": measured_traffic(name, args.layout)},

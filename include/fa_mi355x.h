@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
   FA_DTYPE_FP16 = 0,      /* IEEE binary16 */
@@ -68,7 +68,8 @@ typedef enum {
   FA_ERR_SCALE = -7,      /* scale not finite and positive */
   FA_ERR_CAUSAL = -8,     /* causal not 0 or 1 */
   FA_ERR_LAYOUT = -9,     /* unknown tensor layout */
-  FA_ERR_MIN_KEYS = -10   /* fa_fwd_fp8_pv: min_keys negative */
+  FA_ERR_MIN_KEYS = -10,  /* fa_fwd_fp8_pv: min_keys negative */
+  FA_ERR_WORKSPACE = -11  /* fa_fwd_kvsplit: workspace_bytes too small or negative */
 } fa_status;
 
 /* Memory layout of q, k, v and o (lse is always [B, H, N]). */
@@ -147,6 +148,42 @@ int fa_fwd_fp8_pv(const void* q, const void* k, const void* v,
                   const float* descale_v, void* o, float* lse,
                   int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                   int causal, int layout, int64_t min_keys, void* stream);
+
+/*
+ * fa_fwd_kvsplit_workspace -- bytes of device workspace fa_fwd_kvsplit needs
+ * for this problem: 0 when it would not split (then it runs fa_fwd_ex's
+ * kernels and needs none), otherwise the size of the per-chunk partial
+ * results (fp32).  Arguments as for fa_fwd_ex (the layout does not matter);
+ * invalid ones return the negative fa_status fa_fwd_ex would.
+ */
+int64_t fa_fwd_kvsplit_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
+                                 int causal, int dtype);
+
+/*
+ * fa_fwd_kvsplit -- fa_fwd_ex for grids too small or too unequal to fill the
+ * GPU: few heads, or causal, where the longest query tiles would run alone
+ * at the end (the under-filled launch measured in "TCA 51%，MFU 不足 8%",
+ * section "基于 NCU 进行校验": a 256-block grid on 320 block slots leaves
+ * part of the machine at half load).  The key range of long query tiles is cut into
+ * chunks that separate workgroups process; a second kernel merges them with
+ * LSE = ln sum_c exp(LSE_c) and O = sum_c exp(LSE_c - LSE) O_c, the identity
+ * the LSE output exists for.  Chunks start at or before their tile's first
+ * row, so every row has keys in every chunk.  The library chooses the chunk
+ * size (or no split, when it estimates no gain; then it is fa_fwd_ex); the
+ * result matches fa_fwd_ex within rounding (the merge adds a few fp32
+ * operations per element).  workspace: device memory of at least
+ * fa_fwd_kvsplit_workspace() bytes, 256-byte aligned (FA_ERR_ALIGN), owned
+ * by the caller, contents irrelevant before and after; it may be NULL when
+ * that size is 0 (FA_ERR_NULL otherwise).  workspace_bytes below the
+ * requirement or negative returns FA_ERR_WORKSPACE.  Two kernels are
+ * enqueued when splitting.  Other arguments and errors as for fa_fwd_ex.
+ */
+int fa_fwd_kvsplit(const void* q, const void* k, const void* v,
+                   const float* descale_q, const float* descale_k,
+                   const float* descale_v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                   int causal, int dtype, int layout, void* workspace,
+                   int64_t workspace_bytes, void* stream);
 
 /*
  * fa_bwd -- gradients of the attention forward pass (fp16 or bf16 inputs,

@@ -235,3 +235,72 @@ def test_fa_fwd_fp8_pv_rejects(kw, status):
 def test_fa_fwd_fp8_pv_empty_is_a_noop(min_keys):
     assert _call_pv(min_keys=min_keys, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
     assert _call_pv(min_keys=min_keys, H=0) == 0
+
+
+# --- key-range split: the plan is host logic, visible through the workspace size ---
+
+def _ws(B, H, N, d, causal, dtype):
+    return binding.load_library().fa_fwd_kvsplit_workspace(B, H, N, d, causal, dtype)
+
+
+def test_kvsplit_workspace_follows_the_plan():
+    c = _header_constants()
+    # Grids with at least two tiles per resident workgroup are not split.
+    assert _ws(2, 16, 4096, 128, 0, 0) == 0        # 512 tiles of 256 rows
+    assert _ws(1, 32, 8192, 128, 1, 1) == 0        # 1024 causal tiles
+    assert _ws(1, 32, 16384, 128, 1, 2) == 0       # fp8: 4096 tiles of 128 rows
+    assert _ws(4, 16, 1024, 64, 0, 0) == 0         # 512 tiles, 8 groups each: no gain
+    assert _ws(1, 2, 256, 64, 0, 0) == 0           # fewer than 4 tiles per head
+    # One GPU's share of the bf16 causal workload (4 of 32 heads): 32 tiles of
+    # 256 rows per head, tile t spanning t + 1 groups; chunks of <= 11 groups
+    # give 63 chunks per head (252 workgroups for 256 CUs), the longest tile 3.
+    assert _ws(1, 4, 8192, 128, 1, 1) == 4 * 32 * 3 * 256 * (128 + 1) * 4
+    # Non-causal: split only when even 128-row tiles leave CUs idle.  8 heads
+    # of 4096 rows fill the 256 CUs with 128-row tiles; 4 heads do not:
+    # 16 tiles of 16 groups per head, chunks of 4 groups.
+    assert _ws(1, 8, 4096, 128, 0, 0) == 0
+    assert _ws(1, 16, 2048, 128, 0, 0) == 0
+    assert _ws(1, 4, 4096, 128, 0, 0) == 4 * 16 * 4 * 256 * 129 * 4
+    # Invalid arguments give fa_fwd_ex's statuses; an empty problem needs nothing.
+    assert _ws(1, 4, 8192, 96, 1, 1) == c["FA_ERR_HEAD_DIM"]
+    assert _ws(1, 4, 8192, 128, 2, 1) == c["FA_ERR_CAUSAL"]
+    assert _ws(1, 4, 8192, 128, 1, 9) == c["FA_ERR_DTYPE"]
+    assert _ws(-1, 4, 8192, 128, 1, 1) == c["FA_ERR_SHAPE"]
+    assert _ws(1, 4, 0, 128, 1, 1) == 0
+
+
+def _call_split(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, dq=None, dk=None, dv=None, o=O, lse=L, B=1, H=4, N=8192, d=128,
+                scale=0.1, causal=1, dtype=1, layout=0, ws=A + 0x10000, ws_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    return lib.fa_fwd_kvsplit(args["q"], args["k"], args["v"], args["dq"], args["dk"],
+                              args["dv"], args["o"], args["lse"], args["B"], args["H"],
+                              args["N"], args["d"], args["scale"], args["causal"],
+                              args["dtype"], args["layout"], args["ws"], args["ws_bytes"],
+                              args["stream"])
+
+
+NEED = 4 * 32 * 3 * 256 * 129 * 4  # bf16 causal [1, 4, 8192, 128]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), "FA_ERR_NULL"),
+    (dict(ws=A + 0x10080), "FA_ERR_ALIGN"),
+    (dict(ws_bytes=NEED - 1), "FA_ERR_WORKSPACE"),
+    (dict(ws_bytes=-1), "FA_ERR_WORKSPACE"),
+    (dict(ws_bytes=-1, N=0), "FA_ERR_WORKSPACE"),
+    (dict(layout=5), "FA_ERR_LAYOUT"),
+    (dict(d=80), "FA_ERR_HEAD_DIM"),
+    (dict(scale=0.0), "FA_ERR_SCALE"),
+    (dict(o=None), "FA_ERR_NULL"),
+    (dict(dtype=2, dq=A + 0x5000), "FA_ERR_NULL"),
+])
+def test_fa_fwd_kvsplit_rejects(kw, status):
+    assert _call_split(**kw) == _header_constants()[status]
+
+
+def test_fa_fwd_kvsplit_empty_is_a_noop():
+    assert _call_split(N=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0) == 0
+    assert _call_split(B=0, ws=None, ws_bytes=0) == 0
