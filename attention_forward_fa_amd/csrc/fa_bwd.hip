@@ -223,7 +223,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
   const __amdgpu_buffer_rsrc_t dors = head_rsrc(p.dout + head_off * 2, head_bytes);
 
   const int q0 = qt * kBT;
-  const int my_q = q0 + wave * kRW + lr;
+  const int qw0 = q0 + wave * kRW;  // first query of this wave
+  const int my_q = qw0 + lr;
   const float cs = p.scale * kLog2e;
 
   // Q and dO rows of this lane's query (B operands), and D = dO . O.
@@ -284,21 +285,30 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
     // dS^T = P^T (dP^T - D), P^T = exp2(cs s - lse log2 e); masked pairs give 0.
     uint32_t dsw[2][2][4];
     const int kb0 = j * kBS;
+    float pt[2][16];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float ds[2];
+      for (int i = 0; i < 16; ++i) pt[t2][i] = __builtin_amdgcn_exp2f(fmaf(st[t2][i], cs, -lse_l2));
+    // Only a block reaching past N or past the wave's first query needs the
+    // mask (one uniform branch; exp2 of a masked score is replaced, never used).
+    if (kb0 + kBS > N || (CAUSAL && kb0 + kBS - 1 > qw0)) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int key = kb0 + t2 * 32 + 8 * ((i + e) / 4) + 4 * hh + ((i + e) % 4);
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb0 + t2 * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
           bool keep = key < N;
           if constexpr (CAUSAL) keep = keep && key <= my_q;
-          const float pv = keep ? __builtin_amdgcn_exp2f(fmaf(st[t2][i + e], cs, -lse_l2)) : 0.0f;
-          ds[e] = pv * (dpt[t2][i + e] - dsum);
+          pt[t2][i] = keep ? pt[t2][i] : 0.0f;
         }
-        dsw[t2][i / 8][(i % 8) / 2] = pack2<DT>(ds[0], ds[1]);
-      }
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2)
+        dsw[t2][i / 8][(i % 8) / 2] = pack2<DT>(pt[t2][i] * (dpt[t2][i] - dsum),
+                                                pt[t2][i + 1] * (dpt[t2][i + 1] - dsum));
     __builtin_amdgcn_sched_barrier(0);
     // dQ^T += K^T dS^T.
 #pragma unroll
@@ -442,25 +452,38 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
     // P = exp2(cs s - lse log2 e), dS = P (dP - D); masked pairs give 0.
     // w holds P (PART 1) or dS (PART 2) as pairs of the input type.
     uint32_t w[2][2][4];
+    // Four accumulator rows at a time: elements 4 g .. 4 g + 3 of tile t2 are
+    // query rows t2*32 + 8 g + 4 hh .. +3, whose LSE (and D) are four
+    // consecutive floats.  Only a block reaching past N or below the tile's
+    // last key needs the mask (a uniform branch; exp2 of a masked score is
+    // replaced, never used).
+    const bool edge = qrow0 + kBS > N || (CAUSAL && qrow0 < k0 + kBT);
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float pv[2], ds[2];
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lb + t2 * 32 + 8 * g + 4 * hh);
+        float pt[4];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int ii = i + e;
-          const int qi = qrow0 + t2 * 32 + 8 * (ii / 4) + 4 * hh + (ii % 4);
-          bool keep = qi < N;
-          if constexpr (CAUSAL) keep = keep && qi >= my_k;
-          // Rows 8 g + 4 hh .. +3 of tile t2, which the accumulator holds in
-          // its elements 4 g .. 4 g + 3.
-          const int row = t2 * 32 + 8 * (ii / 4) + 4 * hh + (ii % 4);
-          const float lse = lb[row];
-          pv[e] = keep ? __builtin_amdgcn_exp2f(fmaf(s[t2][ii], cs, -lse * kLog2e)) : 0.0f;
-          if constexpr (!kDV) ds[e] = pv[e] * (dp[t2][ii] - dlb[row]);
+        for (int i = 0; i < 4; ++i)
+          pt[i] = __builtin_amdgcn_exp2f(fmaf(s[t2][4 * g + i], cs, -lse4[i] * kLog2e));
+        if (edge) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int qi = qrow0 + t2 * 32 + 8 * g + 4 * hh + i;
+            bool keep = qi < N;
+            if constexpr (CAUSAL) keep = keep && qi >= my_k;
+            pt[i] = keep ? pt[i] : 0.0f;
+          }
         }
-        w[t2][i / 8][(i % 8) / 2] = kDV ? pack2<DT>(pv[0], pv[1]) : pack2<DT>(ds[0], ds[1]);
+        if constexpr (!kDV) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + t2 * 32 + 8 * g + 4 * hh);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pt[i] *= dp[t2][4 * g + i] - d4[i];
+        }
+        // elements 4 g .. 4 g + 3 go to k-step g / 2, dwords 2 (g % 2), +1
+        w[t2][g / 2][2 * (g % 2)] = pack2<DT>(pt[0], pt[1]);
+        w[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(pt[2], pt[3]);
       }
     __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P, or dK^T += Q^T dS.
