@@ -415,16 +415,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
 
-  // LSE and D rows of a block: wave 0 and wave 1, one dword per lane.
-  auto load_ld = [&](float* lse_dst, float* d_dst, int row0) __attribute__((always_inline)) {
+  // LSE and D rows of a block, one dword per lane: D goes straight to LDS
+  // (wave 1); LSE passes through wave 0's registers to be stored already
+  // multiplied by log2 e, once per row instead of once per score.
+  float lse_next = 0.0f;
+  auto load_ld = [&](float* d_dst, int row0) __attribute__((always_inline)) {
     const int off = (row0 < N ? row0 : N) * 4 + lane * 4;  // past N: zeros
-    if (wave == 0) buffer_to_lds4(lrs, lse_dst, off);
+    if (wave == 0) lse_next = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, off, 0, 0));
     if (wave == 1) buffer_to_lds4(drs, d_dst, off);
+  };
+  auto store_lse = [&](float* lse_dst) __attribute__((always_inline)) {
+    if (wave == 0) lse_dst[lane] = lse_next * kLog2e;
   };
 
   ld.load(qrs, q_lds0, qb_begin * kBS, N);
   ld.load(dors, do_lds0, qb_begin * kBS, N);
-  load_ld(lse_lds0, d_lds0, qb_begin * kBS);
+  load_ld(d_lds0, qb_begin * kBS);
+  store_lse(lse_lds0);
   bwd_barrier();
 
   auto step = [&](int j, const uint8_t* qb, const uint8_t* db, const float* lb, const float* dlb,
@@ -432,7 +439,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
     const int qrow0 = (qb_begin + j) * kBS;  // first query of this block
     ld.load(qrs, qn, qrow0 + kBS, N);
     ld.load(dors, dn, qrow0 + kBS, N);
-    load_ld(ln, dln, qrow0 + kBS);
+    load_ld(dln, qrow0 + kBS);
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
     // w holds P (PART 1) or dS (PART 2) as pairs of the input type.
     uint32_t w[2][2][4];
     // Four accumulator rows at a time: elements 4 g .. 4 g + 3 of tile t2 are
-    // query rows t2*32 + 8 g + 4 hh .. +3, whose LSE (and D) are four
+    // query rows t2*32 + 8 g + 4 hh .. +3, whose LSE log2 e (and D) are four
     // consecutive floats.  Only a block reaching past N or below the tile's
     // last key needs the mask (a uniform branch; exp2 of a masked score is
     // replaced, never used).
@@ -466,7 +473,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
         float pt[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          pt[i] = __builtin_amdgcn_exp2f(fmaf(s[t2][4 * g + i], cs, -lse4[i] * kLog2e));
+          pt[i] = __builtin_amdgcn_exp2f(fmaf(s[t2][4 * g + i], cs, -lse4[i]));
         if (edge) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -497,6 +504,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
           acc[t] = mfma16<DT>(tr_operand<ROWB>(kDV ? db : qb, qa, t, 2 * t2 + sg), b, acc[t]);
         }
     mfma_read_pipeline<4 * NDT, 2, 4>();
+    store_lse(ln);  // the next block's LSE; ln was last read in the previous step
     bwd_barrier();
   };
   for (int j = 0; j < nblk; j += 2) {
