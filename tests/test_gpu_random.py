@@ -1,0 +1,93 @@
+"""Randomised parity: seeded draws of shape, head dimension, dtype, causality,
+layout and entry point (fa_fwd_ex, fa_fwd_fp8_pv, fa_fwd_kvsplit; fa_bwd),
+every output against the CPU fp64 oracle with the bars of the other parity
+tests.  The case lists are fixed by their seeds, so a failure names a case
+that reruns exactly."""
+import numpy as np
+import pytest
+import torch
+
+from attention_forward_fa_amd import binding, inputs
+from tests.test_gpu_parity import announce, check, to_np
+
+pytestmark = pytest.mark.gpu
+
+TORCH = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+
+
+def _cases(n=40, seed=20261202):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = ["fp16", "bf16", "fp8"][rng.integers(3)]
+        entry = ["ex", "kvsplit", "fp8_pv"][rng.integers(3)] if dtype == "fp8" else \
+            ["ex", "kvsplit"][rng.integers(2)]
+        out.append(dict(
+            B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)),
+            N=int(rng.choice([1, 2, 63, 64, 65, 127, 128, 129, 255, 300, 511, 513, 700, 1000,
+                              1299])),
+            d=int(rng.choice([64, 128])), dtype=dtype, causal=bool(rng.integers(2)),
+            layout=["bhnd", "bnhd"][rng.integers(2)], entry=entry,
+            min_keys=int(rng.choice([0, 1, 129, 512])), seed=3000 + i))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: (
+    f"{c['entry']}-{c['dtype']}-B{c['B']}H{c['H']}N{c['N']}d{c['d']}"
+    f"-{'causal' if c['causal'] else 'full'}-{c['layout']}-s{c['seed']}"))
+def test_random_forward(case):
+    inp = inputs.draw(case["B"], case["H"], case["N"], case["d"], case["dtype"], case["causal"],
+                      seed=case["seed"])
+    announce(f"random {case}")
+    q, k, v, ds = binding.to_device(inp)
+    if case["layout"] == "bnhd":
+        q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+    kw = dict(layout=case["layout"], causal=inp.causal, scale=inp.scale,
+              descales=ds if inp.dtype == "fp8" else None)
+    if case["entry"] == "kvsplit":
+        o, l = binding.fwd_kvsplit(q, k, v, **kw)
+    elif case["entry"] == "fp8_pv":
+        o, l = binding.fwd_fp8_pv(q, k, v, min_keys=case["min_keys"], **kw)
+    else:
+        o, l = binding.fwd_ex(q, k, v, **kw)
+    torch.cuda.synchronize()
+    if case["layout"] == "bnhd":
+        o = o.transpose(1, 2).contiguous()
+    on, ln = to_np(o, l, inp)
+    if case["entry"] == "fp8_pv":
+        # Tiles of 128 rows whose first row sees >= min_keys keys take e4m3 P:
+        # those rows get the e4m3 bound of the fp8-P V tests, the rest the
+        # fixed bars.
+        from tests.test_gpu_fp8pv import check_e4m3_bound
+        check_e4m3_bound(inp, on, ln)
+    else:
+        check(inp, on, ln)
+
+
+def _bwd_cases(n=12, seed=20261203):
+    rng = np.random.default_rng(seed)
+    return [dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)),
+                 N=int(rng.choice([1, 5, 64, 65, 127, 129, 200, 333, 513])),
+                 d=int(rng.choice([64, 128])), dtype=["fp16", "bf16"][rng.integers(2)],
+                 causal=bool(rng.integers(2)), seed=3100 + i) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _bwd_cases(), ids=lambda c: (
+    f"bwd-{c['dtype']}-B{c['B']}H{c['H']}N{c['N']}d{c['d']}"
+    f"-{'causal' if c['causal'] else 'full'}-s{c['seed']}"))
+def test_random_backward(case):
+    from tests.test_gpu_bwd import check_grads, run_bwd
+    inp = inputs.draw_bwd(case["B"], case["H"], case["N"], case["d"], case["dtype"],
+                          case["causal"], seed=case["seed"])
+    dq, dk, dv, delta, o = run_bwd(inp)
+    check_grads(inp, (dq, dk, dv))
