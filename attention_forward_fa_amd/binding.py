@@ -42,6 +42,9 @@ SIGNATURES = {
     "fa_fwd_kvsplit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                       ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       _P, _I64, _P]),
+    "fa_fwd_fp8_pv_kvsplit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
+                                             _I64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                             _I64, _P, _I64, _P]),
     "fa_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                               ctypes.c_float, ctypes.c_int, ctypes.c_int, _P]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -279,6 +282,37 @@ def fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str =
                                 _ptr(out), _ptr(lse), B, H, N, d, scale, int(bool(causal)),
                                 _TORCH_DTYPE_CODE[q.dtype], LAYOUTS[layout], _ptr(workspace),
                                 ws_bytes, stream)
+    _check(st)
+    return out, lse
+
+
+def fwd_fp8_pv_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, min_keys: int = 512,
+                       layout: str = "bhnd", causal: bool = False,
+                       scale: Optional[float] = None,
+                       descales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fa_fwd_fp8_pv_kvsplit: fwd_fp8_pv with long tiles' key ranges split over
+    workgroups and merged (workspace as for fwd_kvsplit)."""
+    B, H, N, d = _layout_shape(q, layout)
+    _validate(q, k, v)
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError("fwd_fp8_pv_kvsplit takes float8_e4m3fn q, k, v")
+    dq, dk, dv = _descale_ptrs(q, descales, B, H)
+    out, lse = _outputs(q, out, lse, layout)
+    scale = _default_scale(d) if scale is None else float(scale)
+    need = kvsplit_workspace_bytes(B, H, N, d, causal, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_fwd_fp8_pv_kvsplit(_ptr(q), _ptr(k), _ptr(v), _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _ptr(out), _ptr(lse), B, H, N, d, scale,
+                                       int(bool(causal)), LAYOUTS[layout], int(min_keys),
+                                       _ptr(workspace), ws_bytes, stream)
     _check(st)
     return out, lse
 

@@ -931,6 +931,7 @@ struct MergeParams {
   int split_g;
   int split_cmax;
   int causal;
+  int qt_lo;  // tiles below it were not split (written directly)
 };
 
 template <int D, int BR>
@@ -945,7 +946,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
   const int bh = tile / m.n_qtiles, qt = tile % m.n_qtiles;
   const int groups = m.causal ? qt + 1 : m.n_qtiles;
   const int n = (groups + m.split_g - 1) / m.split_g;
-  if (n < 2) return;  // written by the attention kernel itself
+  if (n < 2 || qt < m.qt_lo) return;  // written by an attention kernel itself
   const int r = (blockIdx.x % WPT) * RPW + threadIdx.x / TPR;
   const int row = qt * BR + r;
   if (row >= m.N) return;
@@ -1158,8 +1159,10 @@ SplitPlan plan_split(int64_t BH, int64_t N, int64_t d, bool causal, int dtype) {
   return pl;
 }
 
-template <int DT, int D, bool CAUSAL>
-int launch_split(Params prm, const SplitPlan& pl, void* ws, hipStream_t stream) {
+// Chunk units of the plan over query tiles [qt_lo, T) (the longest-first
+// order lists tiles from T - 1 down, so a shorter count stops above qt_lo).
+template <int DT, int D, bool CAUSAL, bool PV8 = false>
+int launch_split(Params prm, const SplitPlan& pl, void* ws, hipStream_t stream, int qt_lo = 0) {
   constexpr int W = default_waves<DT, D>();
   using S = Shape<W>;
   prm.n_qtiles = pl.T;
@@ -1168,10 +1171,16 @@ int launch_split(Params prm, const SplitPlan& pl, void* ws, hipStream_t stream) 
   prm.split_cmax = pl.cmax;
   prm.ws_o = static_cast<float*>(ws);
   prm.ws_lse = prm.ws_o + (int64_t)prm.bh * pl.T * pl.cmax * S::br * D;
+  int64_t units = pl.units;
+  if (qt_lo > 0) {  // causal: tile t has ceil((t + 1) / g) chunks
+    units = 0;
+    for (int t = qt_lo; t < pl.T; ++t) units += (t + pl.g) / pl.g;
+    units *= prm.bh;
+  }
   void* args[] = {&prm};
   hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, W, false>),
-      dim3((unsigned)pl.units), dim3(S::threads), args, 0, stream);
+      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, W, PV8>),
+      dim3((unsigned)units), dim3(S::threads), args, 0, stream);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
   MergeParams m;
   m.ws_o = prm.ws_o;
@@ -1185,12 +1194,37 @@ int launch_split(Params prm, const SplitPlan& pl, void* ws, hipStream_t stream) 
   m.split_g = pl.g;
   m.split_cmax = pl.cmax;
   m.causal = CAUSAL ? 1 : 0;
+  m.qt_lo = qt_lo;
   void* margs[] = {&m};
   constexpr int kMergeWgsPerTile = S::br / (256 / (D / 4));
   e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_merge_kernel<D, S::br>),
                       dim3((unsigned)(prm.bh * pl.T * kMergeWgsPerTile)), dim3(256), margs, 0,
                       stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// fp8 P V with the key-range split: tiles whose first row sees fewer than
+// min_keys keys run unsplit with fp16 P V (they are short), the others are
+// split over the fp8-P V kernel (the whole grid when non-causal and N >=
+// min_keys; otherwise fp16 P V split throughout).
+template <int D, bool CAUSAL>
+int launch_pv8_split(const Params& prm, int64_t min_keys, const SplitPlan& pl, void* ws,
+                     hipStream_t stream) {
+  constexpr int DT = FA_DTYPE_FP8_E4M3;
+  constexpr int BR = Shape<4>::br;
+  const int n_t = pl.T;
+  const int64_t mk = min_keys < (int64_t)prm.N + 1 ? min_keys : (int64_t)prm.N + 1;
+  int n_lo;
+  if (CAUSAL)
+    n_lo = mk <= 1 ? 0 : (int)((mk - 1 + BR - 1) / BR);
+  else
+    n_lo = prm.N >= mk ? 0 : n_t;
+  if (n_lo > n_t) n_lo = n_t;
+  if (n_lo == n_t) return launch_split<DT, D, CAUSAL, false>(prm, pl, ws, stream);
+  int st = FA_OK;
+  if (n_lo > 0) st = launch_w<DT, D, CAUSAL, 4, false>(prm, 0, n_lo, stream);
+  if (st == FA_OK) st = launch_split<DT, D, CAUSAL, true>(prm, pl, ws, stream, n_lo);
+  return st;
 }
 
 template <int DT>
@@ -1231,6 +1265,13 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   prm.ws_o = nullptr;
   prm.ws_lse = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (split && split->g > 0 && dtype == FA_DTYPE_FP8_E4M3 && pv8_min_keys >= 0) {
+    if (d == 64)
+      return causal ? launch_pv8_split<64, true>(prm, pv8_min_keys, *split, ws, s)
+                    : launch_pv8_split<64, false>(prm, pv8_min_keys, *split, ws, s);
+    return causal ? launch_pv8_split<128, true>(prm, pv8_min_keys, *split, ws, s)
+                  : launch_pv8_split<128, false>(prm, pv8_min_keys, *split, ws, s);
+  }
   if (split && split->g > 0) {
     switch (dtype) {
       case FA_DTYPE_FP16: return launch_split_dt<FA_DTYPE_FP16>(prm, (int)d, causal, *split, ws, s);
@@ -1353,6 +1394,33 @@ extern "C" int fa_fwd_kvsplit(const void* q, const void* k, const void* v, const
   }
   return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal, dtype,
              layout, stream, -1, &pl, workspace);
+}
+
+extern "C" int fa_fwd_fp8_pv_kvsplit(const void* q, const void* k, const void* v,
+                                     const float* descale_q, const float* descale_k,
+                                     const float* descale_v, void* o, float* lse, int64_t B,
+                                     int64_t H, int64_t N, int64_t d, float scale, int causal,
+                                     int layout, int64_t min_keys, void* workspace,
+                                     int64_t workspace_bytes, void* stream) {
+  bool empty;
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, FA_DTYPE_FP8_E4M3, layout,
+                      &empty);
+  if (st != FA_OK) return st;
+  if (min_keys < 0) return FA_ERR_MIN_KEYS;
+  if (workspace_bytes < 0) return FA_ERR_WORKSPACE;
+  if (empty) return FA_OK;
+  const int given = (descale_q != nullptr) + (descale_k != nullptr) + (descale_v != nullptr);
+  if (given != 0 && given != 3) return FA_ERR_NULL;
+  if (given == 3 && (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
+    return FA_ERR_ALIGN;
+  const SplitPlan pl = plan_split(B * H, N, d, causal != 0, FA_DTYPE_FP8_E4M3);
+  if (pl.g > 0) {
+    if (!workspace) return FA_ERR_NULL;
+    if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
+    if (workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
+  }
+  return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal,
+             FA_DTYPE_FP8_E4M3, layout, stream, min_keys, &pl, workspace);
 }
 
 extern "C" const char* fa_status_string(int status) {

@@ -148,7 +148,11 @@ def time_gpu(inp, steps, warmup, clock=None, layout="bhnd", pv8=None, kvsplit=Fa
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step():
-        if kvsplit:
+        if kvsplit and pv8 is not None and inp.dtype == "fp8":
+            binding.fwd_fp8_pv_kvsplit(q, k, v, min_keys=pv8, layout=layout, causal=inp.causal,
+                                       scale=inp.scale, descales=ds, out=out, lse=lse,
+                                       workspace=ws)
+        elif kvsplit:
             binding.fwd_kvsplit(q, k, v, layout=layout, causal=inp.causal, scale=inp.scale,
                                 descales=ds, out=out, lse=lse, workspace=ws)
         elif pv8 is not None and inp.dtype == "fp8":

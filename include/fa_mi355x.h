@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
   FA_DTYPE_FP16 = 0,      /* IEEE binary16 */
@@ -184,6 +184,23 @@ int fa_fwd_kvsplit(const void* q, const void* k, const void* v,
                    int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                    int causal, int dtype, int layout, void* workspace,
                    int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_fp8_pv_kvsplit -- fa_fwd_fp8_pv with the key-range split of
+ * fa_fwd_kvsplit: query tiles whose first row sees fewer than min_keys keys
+ * (short ones) run unsplit with P V in fp16, the others are split into chunks
+ * with P V on the fp8 matrix instructions, and the chunks are merged through
+ * their LSE.  Accuracy as fa_fwd_fp8_pv (the merge adds fp32 rounding only).
+ * workspace: at least fa_fwd_kvsplit_workspace(B, H, N, d, causal,
+ * FA_DTYPE_FP8_E4M3) bytes, 256-byte aligned, or NULL when that is 0 (then
+ * this is fa_fwd_fp8_pv).  Errors as for fa_fwd_fp8_pv and fa_fwd_kvsplit.
+ */
+int fa_fwd_fp8_pv_kvsplit(const void* q, const void* k, const void* v,
+                          const float* descale_q, const float* descale_k,
+                          const float* descale_v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                          int causal, int layout, int64_t min_keys, void* workspace,
+                          int64_t workspace_bytes, void* stream);
 
 /*
  * fa_bwd -- gradients of the attention forward pass (fp16 or bf16 inputs,

@@ -304,3 +304,35 @@ def test_fa_fwd_kvsplit_rejects(kw, status):
 def test_fa_fwd_kvsplit_empty_is_a_noop():
     assert _call_split(N=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0) == 0
     assert _call_split(B=0, ws=None, ws_bytes=0) == 0
+
+
+def _call_pvsplit(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, dq=None, dk=None, dv=None, o=O, lse=L, B=1, H=4, N=16384, d=128,
+                scale=0.1, causal=1, layout=0, min_keys=512, ws=A + 0x10000, ws_bytes=1 << 34,
+                stream=None)
+    args.update(kw)
+    return lib.fa_fwd_fp8_pv_kvsplit(args["q"], args["k"], args["v"], args["dq"], args["dk"],
+                                     args["dv"], args["o"], args["lse"], args["B"], args["H"],
+                                     args["N"], args["d"], args["scale"], args["causal"],
+                                     args["layout"], args["min_keys"], args["ws"],
+                                     args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(min_keys=-1), "FA_ERR_MIN_KEYS"),
+    (dict(ws_bytes=-5), "FA_ERR_WORKSPACE"),
+    (dict(ws=None), "FA_ERR_NULL"),
+    (dict(ws=A + 0x10010), "FA_ERR_ALIGN"),
+    (dict(ws_bytes=1000), "FA_ERR_WORKSPACE"),
+    (dict(layout=7), "FA_ERR_LAYOUT"),
+    (dict(dq=A + 0x5000, dk=A + 0x6000), "FA_ERR_NULL"),
+    (dict(lse=None), "FA_ERR_NULL"),
+])
+def test_fa_fwd_fp8_pv_kvsplit_rejects(kw, status):
+    assert _call_pvsplit(**kw) == _header_constants()[status]
+
+
+def test_fa_fwd_fp8_pv_kvsplit_empty_is_a_noop():
+    assert _call_pvsplit(N=0, q=None, k=None, v=None, o=None, lse=None, ws=None,
+                         ws_bytes=0) == 0

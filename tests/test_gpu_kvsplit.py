@@ -167,3 +167,57 @@ def test_zero_q_prefix_mean():
     o, l = to_np(*run_split(inp), inp)
     check(inp, o, l)
     assert np.abs(l - np.log(np.arange(1, N + 1))[None, :]).max() <= 1e-3
+
+
+# --- fp8 P V with the split (fa_fwd_fp8_pv_kvsplit) ------------------------------
+
+def run_pv_split(inp, min_keys, layout="bhnd"):
+    announce(f"fa_fwd_fp8_pv_kvsplit min_keys={min_keys} layout={layout} {inp.describe()}")
+    q, k, v, ds = binding.to_device(inp)
+    if layout == "bnhd":
+        q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+    o, l = binding.fwd_fp8_pv_kvsplit(q, k, v, min_keys=min_keys, layout=layout,
+                                      causal=inp.causal, scale=inp.scale, descales=ds)
+    torch.cuda.synchronize()
+    if layout == "bnhd":
+        o = o.transpose(1, 2).contiguous()
+    return o, l
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_pv_split_causal(d):
+    # 12 tiles of 128 rows: tiles 0-3 unsplit with fp16 P V (bit-identical to
+    # fa_fwd_fp8_pv there), tiles 4-11 split with fp8 P V, within the fp8 bars.
+    from tests.test_gpu_fp8pv import run_pv
+    inp = inputs.draw(1, 2, 1500, d, "fp8", True, seed=2700 + d)
+    assert ws_bytes(inp) > 0
+    o, l = run_pv_split(inp, 512)
+    o1, l1 = run_pv(inp, 512)
+    assert torch.equal(o[:, :, :512].contiguous().view(torch.int16),
+                       o1[:, :, :512].contiguous().view(torch.int16))
+    check(inp, *to_np(o, l, inp))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_pv_split_all_tiles_e4m3_bound(causal):
+    from tests.test_gpu_fp8pv import check_e4m3_bound
+    inp = inputs.draw(1, 2, 1500, 128, "fp8", causal, seed=2750)
+    assert ws_bytes(inp) > 0
+    o, l = run_pv_split(inp, 0)
+    check_e4m3_bound(inp, *to_np(o, l, inp))
+
+
+def test_fp8_pv_split_bnhd_matches_bhnd():
+    inp = inputs.draw(1, 3, 1111, 128, "fp8", True, seed=2760)
+    assert ws_bytes(inp) > 0
+    o1, l1 = run_pv_split(inp, 256)
+    o2, l2 = run_pv_split(inp, 256, layout="bnhd")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def test_fp8_pv_split_shard_sampled():
+    inp = inputs.draw_config("fp8_causal_b1h4_n16384_d128")
+    o, l = run_pv_split(inp, 512)
+    rows = np.unique(np.concatenate([_sample_rows(inp.N, seed=2800), [511, 512, 513]]))
+    check(inp, *to_np(o, l, inp), heads=list(range(inp.B * inp.H)), rows=rows)
