@@ -40,6 +40,12 @@
 //     (probabilities then stay <= 2^8 and O, l remain consistent);
 //   * workgroups are mapped to XCDs by head so the query tiles of a head,
 //     which all read the same K and V, share one L2.
+// Further modes of the same kernel: a 4-wave twin of the 8-wave kernels for
+// grids that would leave most CUs idle; fp8 P V (V kept as e4m3 in LDS and
+// read with ds_read_b64_tr_b8, P rounded to e4m3 under a per-row power-of-two
+// scale the MFMA takes back); and a key-range split, where long query tiles'
+// key ranges are cut into chunks over several workgroups and fa_merge_kernel
+// combines the chunks' O and LSE.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -200,7 +206,7 @@ struct Params {
   float* lse;
   int N;
   int H;
-  int n_qtiles;
+  int n_qtiles;  // query tiles of this launch (with the key-range split: of a head)
   int bh;      // B*H
   int layout;  // FA_LAYOUT_BHND or FA_LAYOUT_BNHD (q, k, v and o alike)
   int qt_base; // first query tile of this launch (n_qtiles tiles from there)
