@@ -128,6 +128,8 @@ def _outputs(q, out, lse, layout="bhnd"):
         raise ValueError("out must be a contiguous float16 tensor shaped like q")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if out.device != q.device or lse.device != q.device:
+        raise ValueError("out and lse must be on the device of q, k, v")
     return out, lse
 
 
@@ -258,6 +260,20 @@ def kvsplit_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool, dtype)
     return int(n)
 
 
+def _workspace(workspace, need, device):
+    """The caller's workspace (a contiguous tensor on the inputs' device) and
+    its size in bytes, or one allocated here when none is given."""
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+        raise ValueError("workspace must be a tensor on the device of q, k, v")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bhnd",
                 causal: bool = False, scale: Optional[float] = None,
                 descales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
@@ -272,9 +288,7 @@ def fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str =
     out, lse = _outputs(q, out, lse, layout)
     scale = _default_scale(d) if scale is None else float(scale)
     need = kvsplit_workspace_bytes(B, H, N, d, causal, q.dtype)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
@@ -303,9 +317,7 @@ def fwd_fp8_pv_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, min_ke
     out, lse = _outputs(q, out, lse, layout)
     scale = _default_scale(d) if scale is None else float(scale)
     need = kvsplit_workspace_bytes(B, H, N, d, causal, q.dtype)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream

@@ -570,7 +570,10 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (B == 0 || H == 0 || N == 0) return FA_OK;
-  if (N > (int64_t)1 << 22 || B * H > (int64_t)1 << 24) return FA_ERR_SHAPE;
+  // B and H are bounded one at a time first, so that B * H cannot overflow.
+  if (N > (int64_t)1 << 22 || B > (int64_t)1 << 24 || H > (int64_t)1 << 24 ||
+      B * H > (int64_t)1 << 24)
+    return FA_ERR_SHAPE;
   if (B * H * ((N + kBT - 1) / kBT) > INT32_MAX) return FA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
   if (!aligned_b(q, 16) || !aligned_b(k, 16) || !aligned_b(v, 16) || !aligned_b(o, 16) ||

@@ -1008,7 +1008,10 @@ int check_problem(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int c
   // Index arithmetic: rows of one tensor fit in int32, elements in int64;
   // the grid (B*H query-tile rows) fits in int32.
   // One head's rows must stay addressable by 32-bit buffer offsets.
-  if (N > (int64_t)1 << 22 || B * H > (int64_t)1 << 24) return FA_ERR_SHAPE;
+  // B and H are bounded one at a time first, so that B * H cannot overflow.
+  if (N > (int64_t)1 << 22 || B > (int64_t)1 << 24 || H > (int64_t)1 << 24 ||
+      B * H > (int64_t)1 << 24)
+    return FA_ERR_SHAPE;
   // [B, N, H, d]: one head's rows span N*H*d elements.
   const int64_t esize = dtype == FA_DTYPE_FP8_E4M3 ? 1 : 2;
   if (layout == FA_LAYOUT_BNHD && N * H * d * esize > (int64_t)1 << 30) return FA_ERR_SHAPE;

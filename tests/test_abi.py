@@ -83,6 +83,9 @@ def _call_fp8(**kw):
     (dict(B=-1), "FA_ERR_SHAPE"),
     (dict(N=-5), "FA_ERR_SHAPE"),
     (dict(N=1 << 25), "FA_ERR_SHAPE"),
+    (dict(B=1 << 25), "FA_ERR_SHAPE"),
+    (dict(B=1 << 40, H=1 << 40), "FA_ERR_SHAPE"),  # B * H would overflow int64
+    (dict(B=1 << 13, H=1 << 12), "FA_ERR_SHAPE"),
     (dict(d=96), "FA_ERR_HEAD_DIM"),
     (dict(d=0), "FA_ERR_HEAD_DIM"),
     (dict(dtype=3), "FA_ERR_DTYPE"),
@@ -188,6 +191,7 @@ def _call_bwd(**kw):
     (dict(scale=-1.0), "FA_ERR_SCALE"),
     (dict(N=-1), "FA_ERR_SHAPE"),
     (dict(N=1 << 23), "FA_ERR_SHAPE"),
+    (dict(B=1 << 40, H=1 << 40), "FA_ERR_SHAPE"),  # B * H would overflow int64
     (dict(delta=None), "FA_ERR_NULL"),
     (dict(dv=None), "FA_ERR_NULL"),
     (dict(do=None), "FA_ERR_NULL"),

@@ -221,3 +221,16 @@ def test_fp8_pv_split_shard_sampled():
     o, l = run_pv_split(inp, 512)
     rows = np.unique(np.concatenate([_sample_rows(inp.N, seed=2800), [511, 512, 513]]))
     check(inp, *to_np(o, l, inp), heads=list(range(inp.B * inp.H)), rows=rows)
+
+
+def test_binding_rejects_foreign_workspace():
+    # A workspace in host memory, or strided, is refused before any launch.
+    inp = inputs.draw(1, 2, 1100, 128, "fp16", True, seed=2900)
+    need = ws_bytes(inp)
+    assert need > 0
+    q, k, v, _ = binding.to_device(inp)
+    with pytest.raises(ValueError, match="device"):
+        binding.fwd_kvsplit(q, k, v, causal=True, workspace=torch.empty(need, dtype=torch.uint8))
+    strided = torch.empty(2 * need, dtype=torch.uint8, device="cuda")[::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        binding.fwd_kvsplit(q, k, v, causal=True, workspace=strided)

@@ -85,6 +85,15 @@ def test_small_shapes(dtype, d, causal, N):
     check(inp, o, l)
 
 
+def test_binding_rejects_outputs_on_another_device():
+    inp = inputs.draw(1, 2, 100, 64, "fp16", False, seed=1090)
+    q, k, v, _ = binding.to_device(inp)
+    with pytest.raises(ValueError, match="device"):
+        binding.fwd(q, k, v, out=torch.empty(q.shape, dtype=torch.float16))
+    with pytest.raises(ValueError, match="device"):
+        binding.fwd(q, k, v, lse=torch.empty((1, 2, 100), dtype=torch.float32))
+
+
 def test_config1_full():
     inp = inputs.draw_config(0)
     o, l = to_np(*gpu_run(inp), inp)
