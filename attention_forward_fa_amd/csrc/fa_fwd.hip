@@ -1439,7 +1439,9 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "B, H or N is negative or the problem is too large";
     case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
     case FA_ERR_DTYPE: return "unknown dtype";
-    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIGN:
+      return "q, k, v, o must be 16-byte aligned (fa_bwd: every pointer), lse and descales "
+             "4-byte aligned, a split workspace 256-byte aligned";
     case FA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
     case FA_ERR_SCALE: return "scale must be finite and positive";
     case FA_ERR_CAUSAL: return "causal must be 0 or 1";
