@@ -903,19 +903,45 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
                   acc[t][4 * g + 3] * inv};
       }
     if (hh == 0) p.ws_lse[slot] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
-  } else if (my_q < N) {
-    const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;
-    _Float16* orow = p.o + head_off + (int64_t)my_q * row_elems;
+  } else if (n_chunks == 1) {
+    // O leaves through LDS so that the global stores write whole rows.  The
+    // accumulator gives each lane 4-value pieces of one row, so storing it
+    // directly scatters every instruction over 32 rows; a wave retires only
+    // once its stores have completed, and that held each round of workgroups
+    // for microseconds.  Each wave rounds its 32 x D block to fp16 into a K
+    // stage (free once every wave has passed the barrier), 16-byte chunks
+    // XOR-swizzled by row, reads it back row-major, 16 bytes per lane, and
+    // stores whole rows (D consecutive fp16 values in either layout).
+    constexpr int OROWB = D * 2;     // bytes of one fp16 row of O
+    constexpr int OCH = OROWB / 16;  // 16-byte chunks per row
+    constexpr int OWB = kQW * OROWB;  // bytes of one wave's block
+    constexpr int WPB = KBUF / OWB;  // waves per K stage
+    static_assert(WPB >= 1 && kWaves <= 4 * WPB, "O staging must fit the K stages");
+    barrier();
+    const int ob = wave / WPB;
+    uint8_t* obuf = (ob == 0 ? k_lds0 : ob == 1 ? k_lds1 : ob == 2 ? k_lds2 : k_lds3) +
+                    (wave % WPB) * OWB;
+    const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;  // rows >= N are not stored
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = t * 32 + 8 * g + 4 * hh;
+        const int ch = t * 4 + g;  // chunk of d values t*32 + 8g .. +7; this lane's half: 4*hh ..
         u32x2 w = {pack_f16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv),
                    pack_f16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = w;
+        *reinterpret_cast<u32x2*>(obuf + lr * OROWB + ((ch ^ (lr % OCH)) * 16) + 8 * hh) = w;
       }
-    if (hh == 0) p.lse[(int64_t)bh * N + my_q] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int RPI = kWave / OCH;  // rows per read instruction
+#pragma unroll
+    for (int it = 0; it < kQW / RPI; ++it) {
+      const int r = it * RPI + lane / OCH, ch = lane % OCH;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(obuf + r * OROWB + ((ch ^ (r % OCH)) * 16));
+      if (qw0 + r < N)
+        *reinterpret_cast<u32x4*>(p.o + head_off + (int64_t)(qw0 + r) * row_elems + ch * 8) = x;
+    }
+    if (hh == 0 && my_q < N)
+      p.lse[(int64_t)bh * N + my_q] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
   }
 }
 
