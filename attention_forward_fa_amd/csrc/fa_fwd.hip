@@ -886,24 +886,52 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
 
   // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
-  if (my_q < N && n_chunks > 1) {
+  if (n_chunks > 1) {
     // One chunk of a split key range: O over the chunk's keys (fp32) and its
-    // LSE, for the merge.
-    const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;
-    const int64_t slot =
-        ((int64_t)(bh * p.n_qtiles + qt) * p.split_cmax + chunk) * kBR + (my_q - q0);
-    float* orow = p.ws_o + slot * D;
+    // LSE, for the merge.  Whole rows through LDS as below, in NP passes over
+    // d when a wave's fp32 block does not fit its share of the K stages.
+    constexpr int NP = (kWaves * kQW * D * 4 + 4 * KBUF - 1) / (4 * KBUF);
+    constexpr int DP = D / NP;        // d values per pass
+    constexpr int PROWB = DP * 4;     // bytes of one row of a pass
+    constexpr int PCH = PROWB / 16;   // 16-byte chunks per row
+    constexpr int PWB = kQW * PROWB;  // bytes of one wave's block
+    constexpr int WPB = KBUF / PWB;   // waves per K stage
+    static_assert(DP % 32 == 0 && WPB >= 1 && kWaves <= 4 * WPB, "partials must fit the K stages");
+    barrier();
+    const int ob = wave / WPB;
+    uint8_t* obuf = (ob == 0 ? k_lds0 : ob == 1 ? k_lds1 : ob == 2 ? k_lds2 : k_lds3) +
+                    (wave % WPB) * PWB;
+    const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;  // rows >= N are not stored
+    // The wave's rows are consecutive slots of the chunk's partial block.
+    float* wrows = p.ws_o +
+                   (((int64_t)(bh * p.n_qtiles + qt) * p.split_cmax + chunk) * kBR + (qw0 - q0)) * D;
 #pragma unroll
-    for (int t = 0; t < NDT; ++t)
+    for (int ps = 0; ps < NP; ++ps) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = t * 32 + 8 * g + 4 * hh;
-        *reinterpret_cast<f32x4*>(orow + d0) =
-            f32x4{acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv, acc[t][4 * g + 2] * inv,
-                  acc[t][4 * g + 3] * inv};
+      for (int t = ps * (NDT / NP); t < (ps + 1) * (NDT / NP); ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // d values t*32 + 8g + 4hh .. +3: chunk (t*32 + 8g + 4hh - ps*DP) / 4 of the pass
+          const int ch = (t * 32 + 8 * g - ps * DP) / 4 + hh;
+          *reinterpret_cast<f32x4*>(obuf + lr * PROWB + ((ch ^ (lr % PCH)) * 16)) =
+              f32x4{acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv, acc[t][4 * g + 2] * inv,
+                    acc[t][4 * g + 3] * inv};
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      constexpr int RPI = kWave / PCH;  // rows per read instruction
+#pragma unroll
+      for (int it = 0; it < kQW / RPI; ++it) {
+        const int r = it * RPI + lane / PCH, ch = lane % PCH;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(obuf + r * PROWB + ((ch ^ (r % PCH)) * 16));
+        if (qw0 + r < N) *reinterpret_cast<f32x4*>(wrows + (int64_t)r * D + ps * DP + ch * 4) = x;
       }
-    if (hh == 0) p.ws_lse[slot] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
-  } else if (n_chunks == 1) {
+    }
+    if (hh == 0 && my_q < N) {
+      const int64_t slot =
+          ((int64_t)(bh * p.n_qtiles + qt) * p.split_cmax + chunk) * kBR + (my_q - q0);
+      p.ws_lse[slot] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
+    }
+  } else {
     // O leaves through LDS so that the global stores write whole rows.  The
     // accumulator gives each lane 4-value pieces of one row, so storing it
     // directly scatters every instruction over 32 rows; a wave retires only
