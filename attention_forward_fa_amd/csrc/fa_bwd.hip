@@ -187,6 +187,39 @@ __device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rs, void* 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_dst, 4, voffset, 0, 0, 0);
 }
 
+// Stores one wave's 32 x D fp32 block -- accumulators in the 32x32 MFMA
+// layout (lane l: row l % 32, d values t*32 + 8*(i/4) + 4*(l/32) + i%4 of
+// acc[t][i]), times f -- as whole rows: through the wave's own LDS region buf
+// (32 * D * 4 bytes, 16-byte chunks XOR-swizzled by row), read back
+// row-major, 16 bytes per lane.  Stored straight from the accumulators, each
+// instruction would scatter 16-byte pieces over 32 rows, and a wave retires
+// only once its stores have completed.  rows: row 0 of the block in global
+// memory (rows D floats apart); rows at or past n_rows are not stored.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(const f32x16* acc, float f, uint8_t* buf,
+                                               float* rows, int n_rows, int lane) {
+  constexpr int ROWB = D * 4;      // bytes of one row
+  constexpr int CH = ROWB / 16;    // 16-byte chunks per row
+  constexpr int RPI = kWave / CH;  // rows per read instruction
+  const int lr = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ch = 8 * t + 2 * g + hh;  // d values 4 * ch .. +3
+      *reinterpret_cast<f32x4*>(buf + lr * ROWB + ((ch ^ (lr % CH)) * 16)) =
+          f32x4{acc[t][4 * g] * f, acc[t][4 * g + 1] * f, acc[t][4 * g + 2] * f,
+                acc[t][4 * g + 3] * f};
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / CH, ch = lane % CH;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(buf + r * ROWB + ((ch ^ (r % CH)) * 16));
+    if (r < n_rows) *reinterpret_cast<f32x4*>(rows + (int64_t)r * D + ch * 4) = x;
+  }
+}
+
 __device__ __forceinline__ void bwd_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -328,18 +361,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
     step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
-  if (my_q < N) {
-    float* row = p.dq + head_off + (int64_t)my_q * D;
-#pragma unroll
-    for (int t = 0; t < NDT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = t * 32 + 8 * g + 4 * hh;
-        *reinterpret_cast<float4*>(row + d0) =
-            float4{acc[t][4 * g] * p.scale, acc[t][4 * g + 1] * p.scale,
-                   acc[t][4 * g + 2] * p.scale, acc[t][4 * g + 3] * p.scale};
-      }
-  }
+  // The loop's last barrier has drained every load and LDS access: the K and
+  // V stages (one 32 x D fp32 block each) are free for the row-wise store.
+  static_assert(kBwdWaves == 4 && BLK == kRW * D * 4, "one 32 x D fp32 block per stage");
+  uint8_t* sbuf = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+  store_rows_f32<D>(acc, p.scale, sbuf, p.dq + head_off + (int64_t)qw0 * D, N - qw0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -512,19 +538,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
     step(j + 1, q_lds1, do_lds1, lse_lds1, d_lds1, q_lds0, do_lds0, lse_lds0, d_lds0);
   }
 
-  if (my_k < N) {
-    float* row = (kDV ? p.dv : p.dk) + head_off + (int64_t)my_k * D;
-    const float f = kDV ? 1.0f : p.scale;
-#pragma unroll
-    for (int t = 0; t < NDT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = t * 32 + 8 * g + 4 * hh;
-        *reinterpret_cast<float4*>(row + d0) =
-            float4{acc[t][4 * g] * f, acc[t][4 * g + 1] * f, acc[t][4 * g + 2] * f,
-                   acc[t][4 * g + 3] * f};
-      }
-  }
+  // As in the dQ kernel: the Q and dO stages are free after the loop.
+  static_assert(kBwdWaves == 4 && BLK == kRW * D * 4, "one 32 x D fp32 block per stage");
+  uint8_t* sbuf = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? do_lds0 : do_lds1;
+  const int kw0 = k0 + wave * kRW;
+  store_rows_f32<D>(acc, kDV ? 1.0f : p.scale, sbuf, (kDV ? p.dv : p.dk) + head_off + (int64_t)kw0 * D,
+                    N - kw0, lane);
 }
 
 // ---------------------------------------------------------------------------
