@@ -186,6 +186,7 @@ def time_gpu(inp, steps, warmup, clock=None, layout="bhnd", pv8=None, kvsplit=Fa
 def time_gpu_bwd(inp, steps, warmup):
     """Average seconds per fa_bwd call (the forward's O and LSE computed once
     beforehand), HIP events on the launch stream."""
+    import numpy as np
     import torch
 
     from attention_forward_fa_amd import binding
@@ -193,8 +194,9 @@ def time_gpu_bwd(inp, steps, warmup):
     if inp.dtype not in ("fp16", "bf16"):
         raise SystemExit("the backward pass takes fp16 or bf16 workloads")
     q, k, v, _ = binding.to_device(inp, "cuda")
-    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(inp.seed or 0)).to(
-        q.dtype).to("cuda")
+    # dO drawn by the input recipe, after Q, K, V from the same generator.
+    raw = np.ascontiguousarray(inp.do).view(np.int16)
+    do = torch.from_numpy(raw).to("cuda").view(q.dtype)
     o, lse = binding.fwd(q, k, v, causal=inp.causal, scale=inp.scale)
     torch.cuda.synchronize()
 
@@ -291,7 +293,12 @@ def main(argv=None):
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, args.steps)
     name, B, H, N, d, dtype, causal, seed = inputs.config(args.workload)
-    inp = inputs.draw(B, H, N, d, dtype, causal, seed)
+    if args.which == "bwd":
+        if dtype not in ("fp16", "bf16"):
+            raise SystemExit("the backward pass takes fp16 or bf16 workloads")
+        inp = inputs.draw_bwd(B, H, N, d, dtype, causal, seed)
+    else:
+        inp = inputs.draw(B, H, N, d, dtype, causal, seed)
     if args.which == "bwd":
         # Backward pass: 5 products of 2*N^2*d per head (2.5x the forward count).
         steps, warmup = min(args.steps, 200), min(args.warmup, 100)

@@ -99,6 +99,16 @@ def test_bwd_medium_sampled_heads(dtype, causal):
     check_grads(inp, (dq, dk, dv), heads=[0, 5])
 
 
+@pytest.mark.parametrize("B,H,N,dtype,causal,seed,heads", [
+    (2, 16, 4096, "fp16", False, 3, [0, 31]),   # the workload bench.py --pass bwd times
+    (1, 2, 8192, "bf16", True, 4, [1]),          # the causal workload's N, two of its heads
+])
+def test_bwd_full_size_sampled_heads(B, H, N, dtype, causal, seed, heads):
+    inp = inputs.draw_bwd(B, H, N, 128, dtype, causal, seed=seed)
+    dq, dk, dv, _, _ = run_bwd(inp)
+    check_grads(inp, (dq, dk, dv), heads=heads)
+
+
 def test_bwd_rejects_fp8():
     x = torch.zeros((1, 1, 64, 64), dtype=torch.float16, device="cuda")
     lib = binding.load_library()
