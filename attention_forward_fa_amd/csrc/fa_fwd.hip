@@ -216,11 +216,11 @@ struct Params {
   // in groups of BR/64 blocks (causal tile t: t + 1 groups; otherwise
   // ceil(N / BR)), is cut into ceil(groups / split_g) chunks of near-equal
   // size.  Tiles with one chunk write O and LSE; the others write their
-  // chunk's O (fp32, normalised) and LSE to ws_o / ws_lse, slot
+  // chunk's O (normalised, rounded to fp16) and LSE to ws_o / ws_lse, slot
   // ((bh * n_qtiles + t) * split_cmax + chunk) * BR + row, for the merge.
   int split_g;
   int split_cmax;
-  float* ws_o;
+  _Float16* ws_o;
   float* ws_lse;
 };
 
@@ -886,52 +886,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
 
   // ---- epilogue: O = O^T / l (fp16), LSE = ln 2 * (m c + log2 l) ----------------
   const float l_tot = sum_pair32(l_run);
-  if (n_chunks > 1) {
-    // One chunk of a split key range: O over the chunk's keys (fp32) and its
-    // LSE, for the merge.  Whole rows through LDS as below, in NP passes over
-    // d when a wave's fp32 block does not fit its share of the K stages.
-    constexpr int NP = (kWaves * kQW * D * 4 + 4 * KBUF - 1) / (4 * KBUF);
-    constexpr int DP = D / NP;        // d values per pass
-    constexpr int PROWB = DP * 4;     // bytes of one row of a pass
-    constexpr int PCH = PROWB / 16;   // 16-byte chunks per row
-    constexpr int PWB = kQW * PROWB;  // bytes of one wave's block
-    constexpr int WPB = KBUF / PWB;   // waves per K stage
-    static_assert(DP % 32 == 0 && WPB >= 1 && kWaves <= 4 * WPB, "partials must fit the K stages");
-    barrier();
-    const int ob = wave / WPB;
-    uint8_t* obuf = (ob == 0 ? k_lds0 : ob == 1 ? k_lds1 : ob == 2 ? k_lds2 : k_lds3) +
-                    (wave % WPB) * PWB;
-    const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;  // rows >= N are not stored
-    // The wave's rows are consecutive slots of the chunk's partial block.
-    float* wrows = p.ws_o +
-                   (((int64_t)(bh * p.n_qtiles + qt) * p.split_cmax + chunk) * kBR + (qw0 - q0)) * D;
-#pragma unroll
-    for (int ps = 0; ps < NP; ++ps) {
-#pragma unroll
-      for (int t = ps * (NDT / NP); t < (ps + 1) * (NDT / NP); ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // d values t*32 + 8g + 4hh .. +3: chunk (t*32 + 8g + 4hh - ps*DP) / 4 of the pass
-          const int ch = (t * 32 + 8 * g - ps * DP) / 4 + hh;
-          *reinterpret_cast<f32x4*>(obuf + lr * PROWB + ((ch ^ (lr % PCH)) * 16)) =
-              f32x4{acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv, acc[t][4 * g + 2] * inv,
-                    acc[t][4 * g + 3] * inv};
-        }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      constexpr int RPI = kWave / PCH;  // rows per read instruction
-#pragma unroll
-      for (int it = 0; it < kQW / RPI; ++it) {
-        const int r = it * RPI + lane / PCH, ch = lane % PCH;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(obuf + r * PROWB + ((ch ^ (r % PCH)) * 16));
-        if (qw0 + r < N) *reinterpret_cast<f32x4*>(wrows + (int64_t)r * D + ps * DP + ch * 4) = x;
-      }
-    }
-    if (hh == 0 && my_q < N) {
-      const int64_t slot =
-          ((int64_t)(bh * p.n_qtiles + qt) * p.split_cmax + chunk) * kBR + (my_q - q0);
-      p.ws_lse[slot] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
-    }
-  } else {
+  {
     // O leaves through LDS so that the global stores write whole rows.  The
     // accumulator gives each lane 4-value pieces of one row, so storing it
     // directly scatters every instruction over 32 rows; a wave retires only
@@ -939,12 +894,28 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     // for microseconds.  Each wave rounds its 32 x D block to fp16 into a K
     // stage (free once every wave has passed the barrier), 16-byte chunks
     // XOR-swizzled by row, reads it back row-major, 16 bytes per lane, and
-    // stores whole rows (D consecutive fp16 values in either layout).
+    // stores whole rows (D consecutive fp16 values in either layout).  One
+    // chunk of a split key range stores its rows (O over the chunk's keys) and
+    // LSE the same way to its slots of the workspace, for the merge.
     constexpr int OROWB = D * 2;     // bytes of one fp16 row of O
     constexpr int OCH = OROWB / 16;  // 16-byte chunks per row
     constexpr int OWB = kQW * OROWB;  // bytes of one wave's block
     constexpr int WPB = KBUF / OWB;  // waves per K stage
     static_assert(WPB >= 1 && kWaves <= 4 * WPB, "O staging must fit the K stages");
+    _Float16* wrows;  // row 0 of this wave's block
+    int64_t wstride;  // elements between its rows
+    float* wlse;      // LSE of row 0
+    if (n_chunks > 1) {
+      const int64_t slot0 =
+          ((int64_t)(bh * p.n_qtiles + qt) * p.split_cmax + chunk) * kBR + (qw0 - q0);
+      wrows = p.ws_o + slot0 * D;
+      wstride = D;
+      wlse = p.ws_lse + slot0;
+    } else {
+      wrows = p.o + head_off + (int64_t)qw0 * row_elems;
+      wstride = row_elems;
+      wlse = p.lse + (int64_t)bh * N + qw0;
+    }
     barrier();
     const int ob = wave / WPB;
     uint8_t* obuf = (ob == 0 ? k_lds0 : ob == 1 ? k_lds1 : ob == 2 ? k_lds2 : k_lds3) +
@@ -965,11 +936,9 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     for (int it = 0; it < kQW / RPI; ++it) {
       const int r = it * RPI + lane / OCH, ch = lane % OCH;
       const u32x4 x = *reinterpret_cast<const u32x4*>(obuf + r * OROWB + ((ch ^ (r % OCH)) * 16));
-      if (qw0 + r < N)
-        *reinterpret_cast<u32x4*>(p.o + head_off + (int64_t)(qw0 + r) * row_elems + ch * 8) = x;
+      if (qw0 + r < N) *reinterpret_cast<u32x4*>(wrows + r * wstride + ch * 8) = x;
     }
-    if (hh == 0 && my_q < N)
-      p.lse[(int64_t)bh * N + my_q] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
+    if (hh == 0 && my_q < N) wlse[lr] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
   }
 }
 
@@ -980,7 +949,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
 // fp16.
 // ---------------------------------------------------------------------------
 struct MergeParams {
-  const float* ws_o;
+  const _Float16* ws_o;
   const float* ws_lse;
   _Float16* o;
   float* lse;
@@ -1020,9 +989,11 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
   for (int ch = 0; ch < n; ++ch) {
     const int64_t slot = slot0 + (int64_t)ch * BR;
     const float w = __expf(m.ws_lse[slot] - mx);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(m.ws_o + slot * D + e0);
+    // One 8-byte load converted as a vector (a __builtin_bit_cast of a single
+    // element of a loaded u32x2 read element 0 twice with this compiler).
+    const f16x4 x = *reinterpret_cast<const f16x4*>(m.ws_o + slot * D + e0);
     wsum += w;
-    acc += w * x;
+    acc += w * __builtin_convertvector(x, f32x4);
   }
   const float inv = 1.0f / wsum;
   int64_t off;
@@ -1188,7 +1159,7 @@ SplitPlan plan_split(int64_t BH, int64_t N, int64_t d, bool causal, int dtype) {
   };
   const double rate = (dtype == FA_DTYPE_FP8_E4M3 ? 1.3e15 : 1.0e15) * (d == 64 ? 0.6 : 1.0);
   const double t_group = 4.0 * br * br * (double)d / (rate / (double)slots);  // seconds
-  const double t_partial = 2.0 * br * (d + 1) * 4.0 / 5e12;                  // seconds per chunk
+  const double t_partial = 2.0 * br * (2.0 * d + 4.0) / 5e12;  // write + read of a chunk's partial, seconds
   const int64_t total = causal ? BH * T * (T + 1) / 2 : BH * T * T;
   double whole;
   if (br == 256 && 2 * BH * T <= kCUs) {  // launch_t runs the 4-wave twin
@@ -1218,7 +1189,7 @@ SplitPlan plan_split(int64_t BH, int64_t N, int64_t d, bool causal, int dtype) {
   }
   pl.cmax = (int)((T + pl.g - 1) / pl.g);
   pl.units = BH * chunks_per_head(pl.g);
-  pl.ws_bytes = BH * T * pl.cmax * br * (d + 1) * (int64_t)sizeof(float);
+  pl.ws_bytes = BH * T * pl.cmax * br * (2 * d + 4);  // O fp16 + LSE fp32 per chunk row
   return pl;
 }
 
@@ -1232,8 +1203,8 @@ int launch_split(Params prm, const SplitPlan& pl, void* ws, hipStream_t stream, 
   prm.qt_base = 0;
   prm.split_g = pl.g;
   prm.split_cmax = pl.cmax;
-  prm.ws_o = static_cast<float*>(ws);
-  prm.ws_lse = prm.ws_o + (int64_t)prm.bh * pl.T * pl.cmax * S::br * D;
+  prm.ws_o = static_cast<_Float16*>(ws);
+  prm.ws_lse = reinterpret_cast<float*>(prm.ws_o + (int64_t)prm.bh * pl.T * pl.cmax * S::br * D);
   int64_t units = pl.units;
   if (qt_lo > 0) {  // causal: tile t has ceil((t + 1) / g) chunks
     units = 0;

@@ -153,7 +153,8 @@ int fa_fwd_fp8_pv(const void* q, const void* k, const void* v,
  * fa_fwd_kvsplit_workspace -- bytes of device workspace fa_fwd_kvsplit needs
  * for this problem: 0 when it would not split (then it runs fa_fwd_ex's
  * kernels and needs none), otherwise the size of the per-chunk partial
- * results (fp32).  Arguments as for fa_fwd_ex (the layout does not matter);
+ * results (O rounded to fp16, LSE in fp32).  Arguments as for fa_fwd_ex (the
+ * layout does not matter);
  * invalid ones return the negative fa_status fa_fwd_ex would.
  */
 int64_t fa_fwd_kvsplit_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
@@ -170,8 +171,9 @@ int64_t fa_fwd_kvsplit_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
  * the LSE output exists for.  Chunks start at or before their tile's first
  * row, so every row has keys in every chunk.  The library chooses the chunk
  * size (or no split, when it estimates no gain; then it is fa_fwd_ex); the
- * result matches fa_fwd_ex within rounding (the merge adds a few fp32
- * operations per element).  workspace: device memory of at least
+ * result matches fa_fwd_ex within rounding (each chunk's O is rounded to
+ * fp16 once before the merge, which then adds a few fp32 operations per
+ * element).  workspace: device memory of at least
  * fa_fwd_kvsplit_workspace() bytes, 256-byte aligned (FA_ERR_ALIGN), owned
  * by the caller, contents irrelevant before and after; it may be NULL when
  * that size is 0 (FA_ERR_NULL otherwise).  workspace_bytes below the
@@ -190,7 +192,8 @@ int fa_fwd_kvsplit(const void* q, const void* k, const void* v,
  * fa_fwd_kvsplit: query tiles whose first row sees fewer than min_keys keys
  * (short ones) run unsplit with P V in fp16, the others are split into chunks
  * with P V on the fp8 matrix instructions, and the chunks are merged through
- * their LSE.  Accuracy as fa_fwd_fp8_pv (the merge adds fp32 rounding only).
+ * their LSE.  Accuracy as fa_fwd_fp8_pv, plus the fp16 rounding of each
+ * chunk's O before the merge.
  * workspace: at least fa_fwd_kvsplit_workspace(B, H, N, d, causal,
  * FA_DTYPE_FP8_E4M3) bytes, 256-byte aligned, or NULL when that is 0 (then
  * this is fa_fwd_fp8_pv).  Errors as for fa_fwd_fp8_pv and fa_fwd_kvsplit.

@@ -258,13 +258,14 @@ def test_kvsplit_workspace_follows_the_plan():
     # One GPU's share of the bf16 causal workload (4 of 32 heads): 32 tiles of
     # 256 rows per head, tile t spanning t + 1 groups; chunks of <= 11 groups
     # give 63 chunks per head (252 workgroups for 256 CUs), the longest tile 3.
-    assert _ws(1, 4, 8192, 128, 1, 1) == 4 * 32 * 3 * 256 * (128 + 1) * 4
+    # Per chunk row: O in fp16 (2 d bytes) and LSE in fp32 (4 bytes).
+    assert _ws(1, 4, 8192, 128, 1, 1) == 4 * 32 * 3 * 256 * (2 * 128 + 4)
     # Non-causal: split only when even 128-row tiles leave CUs idle.  8 heads
     # of 4096 rows fill the 256 CUs with 128-row tiles; 4 heads do not:
     # 16 tiles of 16 groups per head, chunks of 4 groups.
     assert _ws(1, 8, 4096, 128, 0, 0) == 0
     assert _ws(1, 16, 2048, 128, 0, 0) == 0
-    assert _ws(1, 4, 4096, 128, 0, 0) == 4 * 16 * 4 * 256 * 129 * 4
+    assert _ws(1, 4, 4096, 128, 0, 0) == 4 * 16 * 4 * 256 * (2 * 128 + 4)
     # Invalid arguments give fa_fwd_ex's statuses; an empty problem needs nothing.
     assert _ws(1, 4, 8192, 96, 1, 1) == c["FA_ERR_HEAD_DIM"]
     assert _ws(1, 4, 8192, 128, 2, 1) == c["FA_ERR_CAUSAL"]
@@ -286,7 +287,7 @@ def _call_split(**kw):
                               args["stream"])
 
 
-NEED = 4 * 32 * 3 * 256 * 129 * 4  # bf16 causal [1, 4, 8192, 128]
+NEED = 4 * 32 * 3 * 256 * (2 * 128 + 4)  # bf16 causal [1, 4, 8192, 128]: O fp16 + LSE fp32 per chunk row
 
 
 @pytest.mark.parametrize("kw,status", [
