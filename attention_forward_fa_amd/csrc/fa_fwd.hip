@@ -1133,8 +1133,9 @@ int launch_dt(const Params& prm, int d, int causal, hipStream_t stream) {
 // the work per slot, whichever is larger -- for an 8-wave grid small enough
 // to run on the 4-wave twin, with the twin's 128-row tiles (half a group row
 // each) at about 0.8 of the 8-wave rate.  The split is taken when estimated
-// at least 20 % faster; grids with at least two tiles per slot are left whole
-// (the longest-first order balances them).
+// at least 5 % faster (the estimate has erred on the slow side: shapes
+// estimated 5-15 % faster ran 5-9 % faster); grids with at least two tiles
+// per slot are left whole (the longest-first order balances them).
 struct SplitPlan {
   int g = 0;     // chunk size in groups; 0: no split
   int cmax = 0;  // chunks of the longest tile
@@ -1183,7 +1184,7 @@ SplitPlan plan_split(int64_t BH, int64_t N, int64_t d, bool causal, int dtype) {
       pl.g = (int)g;
     }
   }
-  if (pl.g == 0 || best > 0.8 * whole) {
+  if (pl.g == 0 || best > 0.95 * whole) {
     pl.g = 0;
     return pl;
   }

@@ -260,10 +260,11 @@ def test_kvsplit_workspace_follows_the_plan():
     # give 63 chunks per head (252 workgroups for 256 CUs), the longest tile 3.
     # Per chunk row: O in fp16 (2 d bytes) and LSE in fp32 (4 bytes).
     assert _ws(1, 4, 8192, 128, 1, 1) == 4 * 32 * 3 * 256 * (2 * 128 + 4)
-    # Non-causal: split only when even 128-row tiles leave CUs idle.  8 heads
-    # of 4096 rows fill the 256 CUs with 128-row tiles; 4 heads do not:
-    # 16 tiles of 16 groups per head, chunks of 4 groups.
-    assert _ws(1, 8, 4096, 128, 0, 0) == 0
+    # Non-causal: split only when the whole grid leaves CUs idle.  8 heads of
+    # 4096 rows (128 tiles of 256 rows) split in two chunks per tile; 16 heads
+    # of 2048 rows are estimated no faster split; 4 heads of 4096 rows: 16
+    # tiles of 16 groups per head, chunks of 4 groups.
+    assert _ws(1, 8, 4096, 128, 0, 0) == 8 * 16 * 2 * 256 * (2 * 128 + 4)
     assert _ws(1, 16, 2048, 128, 0, 0) == 0
     assert _ws(1, 4, 4096, 128, 0, 0) == 4 * 16 * 4 * 256 * (2 * 128 + 4)
     # Invalid arguments give fa_fwd_ex's statuses; an empty problem needs nothing.
