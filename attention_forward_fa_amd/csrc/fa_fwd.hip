@@ -963,14 +963,21 @@ struct MergeParams {
   int qt_lo;  // tiles below it were not split (written directly)
 };
 
+constexpr int kMergeEPT = 8;  // d values per merge thread: one 16-byte fp16 load per chunk
+
+// Workgroups of 256 threads the merge launches per query tile of BR rows.
+template <int D, int BR>
+constexpr int merge_wgs_per_tile() { return BR / (256 / (D / kMergeEPT)); }
+
 template <int D, int BR>
 __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
-  // One thread per row and 4 d values, so every load of a row's chunks is
+  // One thread per row and 8 d values, so every load of a row's chunks is
   // independent and many are in flight: the merge is a pass over the partials
-  // at memory speed.
-  constexpr int TPR = D / 4;          // threads per row
+  // at memory speed, 16 bytes per load.
+  constexpr int TPR = D / kMergeEPT;  // threads per row
   constexpr int RPW = 256 / TPR;      // rows per workgroup
   constexpr int WPT = BR / RPW;       // workgroups per tile
+  static_assert(WPT == merge_wgs_per_tile<D, BR>(), "merge grid");
   const int tile = blockIdx.x / WPT;  // bh * n_qtiles + qt
   const int bh = tile / m.n_qtiles, qt = tile % m.n_qtiles;
   const int groups = m.causal ? qt + 1 : m.n_qtiles;
@@ -979,21 +986,21 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
   const int r = (blockIdx.x % WPT) * RPW + threadIdx.x / TPR;
   const int row = qt * BR + r;
   if (row >= m.N) return;
-  const int e0 = (threadIdx.x % TPR) * 4;
+  const int e0 = (threadIdx.x % TPR) * kMergeEPT;
   const int64_t slot0 = (int64_t)tile * m.split_cmax * BR + r;  // chunk c: slot0 + c * BR
   float mx = -INFINITY;
   for (int ch = 0; ch < n; ++ch) mx = fmaxf(mx, m.ws_lse[slot0 + (int64_t)ch * BR]);
   float wsum = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x8 acc = {};
 #pragma unroll 4
   for (int ch = 0; ch < n; ++ch) {
     const int64_t slot = slot0 + (int64_t)ch * BR;
     const float w = __expf(m.ws_lse[slot] - mx);
-    // One 8-byte load converted as a vector (a __builtin_bit_cast of a single
-    // element of a loaded u32x2 read element 0 twice with this compiler).
-    const f16x4 x = *reinterpret_cast<const f16x4*>(m.ws_o + slot * D + e0);
+    // One 16-byte load converted as a vector (a __builtin_bit_cast of a single
+    // element of a loaded vector read element 0 with this compiler).
+    const f16x8 x = *reinterpret_cast<const f16x8*>(m.ws_o + slot * D + e0);
     wsum += w;
-    acc += w * __builtin_convertvector(x, f32x4);
+    acc += w * __builtin_convertvector(x, f32x8);
   }
   const float inv = 1.0f / wsum;
   int64_t off;
@@ -1004,8 +1011,10 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
     off = ((int64_t)bh * m.N + row) * D;
   }
   _Float16* dst = m.o + off + e0;
-  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_f16x2(acc[0] * inv, acc[1] * inv),
-                                         pack_f16x2(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x4*>(dst) = u32x4{pack_f16x2(acc[0] * inv, acc[1] * inv),
+                                         pack_f16x2(acc[2] * inv, acc[3] * inv),
+                                         pack_f16x2(acc[4] * inv, acc[5] * inv),
+                                         pack_f16x2(acc[6] * inv, acc[7] * inv)};
   if (e0 == 0) m.lse[(int64_t)bh * m.N + row] = mx + __logf(wsum);
 }
 
@@ -1231,7 +1240,7 @@ int launch_split(Params prm, const SplitPlan& pl, void* ws, hipStream_t stream, 
   m.causal = CAUSAL ? 1 : 0;
   m.qt_lo = qt_lo;
   void* margs[] = {&m};
-  constexpr int kMergeWgsPerTile = S::br / (256 / (D / 4));
+  constexpr int kMergeWgsPerTile = merge_wgs_per_tile<D, S::br>();
   e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_merge_kernel<D, S::br>),
                       dim3((unsigned)(prm.bh * pl.T * kMergeWgsPerTile)), dim3(256), margs, 0,
                       stream);
