@@ -1089,11 +1089,19 @@ int launch_all(const Params& prm, hipStream_t stream) {
 template <int DT, int D, bool CAUSAL>
 int launch_t(const Params& prm, hipStream_t stream) {
   constexpr int W = default_waves<DT, D>();
+  const int64_t wgs8 = (int64_t)prm.bh * ((prm.N + Shape<8>::br - 1) / Shape<8>::br);
   if constexpr (W == 8) {
     // With 256-row tiles filling at most half the CUs, 128-row tiles on all of
     // them finish sooner although one wave per SIMD runs slower than two.
-    const int64_t wgs = (int64_t)prm.bh * ((prm.N + Shape<8>::br - 1) / Shape<8>::br);
-    if (2 * wgs <= kCUs) return launch_all<DT, D, CAUSAL, 4>(prm, stream);
+    if (2 * wgs8 <= kCUs) return launch_all<DT, D, CAUSAL, 4>(prm, stream);
+  }
+  if constexpr (D == 64 && DT != FA_DTYPE_FP8_E4M3 && !CAUSAL) {
+    // Non-causal d = 64 with tiles of 16 or more key blocks: one 8-wave
+    // workgroup per CU (one K/V staging for 256 rows) beats three 4-wave ones
+    // (fp16 [4,16,1024,64] 26.0 -> 24.9 us, [2,16,4096,64] 178 -> 171 us); with
+    // 8 blocks ([16,32,512,64] 53 -> 58 us) or causal tiles the three
+    // co-resident 4-wave workgroups hide the per-tile cost better.
+    if (prm.N >= 1024 && 2 * wgs8 > kCUs) return launch_all<DT, D, CAUSAL, 8>(prm, stream);
   }
   return launch_all<DT, D, CAUSAL, W>(prm, stream);
 }

@@ -133,6 +133,16 @@ def test_eight_wave_kernel_ragged(dtype, causal):
     check(inp, o, l, heads=[0, 1, 16, 32], rows=rows)
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_eight_wave_kernel_d64_ragged(dtype):
+    # Non-causal d = 64 with N >= 1024 and B*H*ceil(N/256) = 200 workgroups:
+    # the 8-wave kernel at d = 64, ragged last tile and last key block.
+    inp = inputs.draw(2, 20, 1100, 64, dtype, False, seed=33)
+    o, l = to_np(*gpu_run(inp), inp)
+    rows = np.unique(np.concatenate([_sample_rows(inp.N, seed=33), [1023, 1024, 1099]]))
+    check(inp, o, l, heads=[0, 7, 21, 39], rows=rows)
+
+
 # --- edge cases and closed forms -----------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
