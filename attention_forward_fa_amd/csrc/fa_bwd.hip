@@ -7,25 +7,27 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernel launches, in this order on the caller's stream:
+// Two kernel launches, in this order on the caller's stream:
 //   * fa_bwd_dq: one workgroup per (b, h, 128-query tile), a wave per 32
 //     queries, shaped like the forward: S^T = K Q^T and dP^T = V dO^T with Q
 //     and dO held in registers as B operands, dS^T in registers, then
 //     dQ^T += K^T dS^T with K^T read transposed (ds_read_b64_tr_b16) from the
 //     row-major K block in LDS.  It also computes D_i for its queries from O
 //     and dO and stores it (delta), for the second kernel.
-//   * fa_bwd_dkdv, twice (dV, then dK): one workgroup per (b, h, 128-key
-//     tile), a wave per 32 keys held in registers (K, and V for dK, rows as
-//     B operands): S = Q K^T (and dP = dO V^T) per 64-query block, then
-//     dV^T += dO^T P, or dK^T += Q^T dS, with dO^T / Q^T read transposed
-//     from the row-major dO / Q blocks.
+//   * fa_bwd_dkdv: one workgroup per (b, h, 128-key tile), two waves per 32
+//     keys: a P wave holds the keys' K rows, computes S = Q K^T and P per
+//     64-query block, dV^T += dO^T P, and passes P through LDS to the dS wave,
+//     which holds the V rows, computes dP = dO V^T, dS = P (dP - D) and
+//     dK^T += Q^T dS; dO^T / Q^T are read transposed from the row-major
+//     dO / Q blocks.
 // Blocks stream global -> LDS (buffer_load ... lds, XOR-swizzled 16-byte
 // chunks) into two buffers, one barrier per block; the loops are unrolled by
 // two so each buffer is its own LDS array.  Rows past N read as zeros and are
 // masked, as are causal pairs (key j > query i); a loop runs to an even block
 // count, the extra block fully masked.  P and dS enter the second products
-// in the input type (fp16 or bf16, round to nearest even); all accumulation
-// is fp32 and the gradients are stored as fp32.
+// in the input type (fp16 or bf16, round to nearest even); the dK kernel's dS
+// is formed from that rounded P, the dQ kernel's from P in fp32.  All
+// accumulation is fp32 and the gradients are stored as fp32.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -154,19 +156,19 @@ __device__ __forceinline__ u32x4 tr_operand(const uint8_t* blk, const BlockAddr<
 // land at row * ROWB with swizzled chunks; one 64-lane load instruction fills
 // 1 KB, the workgroup's waves share the instructions.  Rows at or past N,
 // and blocks past `end_row`, read zeros (the latter without memory traffic).
-template <int ROWB>
+template <int ROWB, int W = kBwdWaves>
 struct BlockLoader {
   static constexpr int CPR = ROWB / 16;
   static constexpr int INSTR = kBS * CPR / kWave;
-  static_assert(INSTR % kBwdWaves == 0, "block must split evenly over the waves");
-  static constexpr int PER_W = INSTR / kBwdWaves;
+  static_assert(INSTR % W == 0, "block must split evenly over the waves");
+  static constexpr int PER_W = INSTR / W;
   int goff[PER_W];
   int wave;
   __device__ __forceinline__ void init(int w, int lane) {
     wave = w;
 #pragma unroll
     for (int u = 0; u < PER_W; ++u) {
-      const int slot = (u * kBwdWaves + w) * kWave + lane;
+      const int slot = (u * W + w) * kWave + lane;
       const int row = slot / CPR, phys = slot % CPR;
       goff[u] = row * ROWB + ((phys ^ swz<ROWB>(row)) * 16);
     }
@@ -176,7 +178,7 @@ struct BlockLoader {
     const int boff = row0 < end_row ? row0 * ROWB : (1 << 30);
 #pragma unroll
     for (int u = 0; u < PER_W; ++u)
-      buffer_to_lds16(rs, blk + (u * kBwdWaves + wave) * kWave * 16, goff[u] + boff, 0);
+      buffer_to_lds16(rs, blk + (u * W + wave) * kWave * 16, goff[u] + boff, 0);
   }
 };
 
@@ -369,19 +371,29 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV.  PART 1 computes dV alone (S, P, dV^T += dO^T P), PART 2 dK
-// alone (S, dP, dS, dK^T += Q^T dS): recomputing S twice costs one product
-// more than both in one kernel, but each half fits two waves per SIMD in
-// the register file, where the fused kernel runs one.
+// dK and dV in one pass over the query blocks, by two kinds of wave per
+// 32-key group: the P wave computes S = Q K^T, P and dV^T += dO^T P, and hands
+// P (in the input type) to the group's dS wave through LDS; the dS wave
+// computes dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS.  Four products per
+// block, where a dV pass and a dK pass of their own would take five (S twice);
+// each wave holds one key operand and one accumulator, so all eight fit two
+// waves per SIMD, and the two kinds' VALU work lands in different halves of
+// the block, beside the other kind's matrix instructions.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool CAUSAL, int PART>
-__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p) {
-  static_assert(PART == 1 || PART == 2, "dV (1) or dK (2)");
-  constexpr bool kDV = PART == 1;
+constexpr int kKVWaves = 2 * kBwdWaves;  // waves 0-3: P, 4-7: dS, of key group wave % 4
+constexpr int kKVThreads = kWave * kKVWaves;
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int ROWB = D * 2;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
   constexpr int BLK = kBS * ROWB;
+  constexpr int PBLK = kRW * kBS * 2;  // one group's P block in the input type
   __shared__ __attribute__((aligned(16))) uint8_t q_lds0[BLK];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds1[BLK];
   __shared__ __attribute__((aligned(16))) uint8_t do_lds0[BLK];
@@ -391,11 +403,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
   __shared__ __attribute__((aligned(16))) float lse_lds1[kBS];
   __shared__ __attribute__((aligned(16))) float d_lds0[kBS];
   __shared__ __attribute__((aligned(16))) float d_lds1[kBS];
+  // P of each key group, from its P wave to its dS wave: lane l's 16 dwords
+  // as four 16-byte pieces at (c * 64 + l) * 16, c = 0 .. 3.
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[kBwdWaves][PBLK];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lr = lane & 31, hh = lane >> 5;
+  const bool pw = wave < kBwdWaves;  // P wave, else dS wave (wave-uniform)
+  const int grp = wave % kBwdWaves;
 
   // Causal work shrinks with the key tile: tile_of hands out its heavy-first
   // order in reverse tile index, so turn it around.
@@ -406,8 +423,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
   const int64_t head_off = (int64_t)bh * N * D;
   const int head_bytes = N * ROWB;
   const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k + head_off * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v + head_off * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t kvrs = head_rsrc((pw ? p.k : p.v) + head_off * 2, head_bytes);
   const __amdgpu_buffer_rsrc_t dors = head_rsrc(p.dout + head_off * 2, head_bytes);
   const __amdgpu_buffer_rsrc_t lrs = head_rsrc(
       reinterpret_cast<const uint8_t*>(p.lse + (int64_t)bh * N), N * 4);
@@ -415,21 +431,19 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
       reinterpret_cast<const uint8_t*>(p.delta + (int64_t)bh * N), N * 4);
 
   const int k0 = kt * kBT;
-  const int my_k = k0 + wave * kRW + lr;
+  const int my_k = k0 + grp * kRW + lr;
   const float cs = p.scale * kLog2e;
 
-  // K and V rows of this lane's key (B operands of S = Q K^T, dP = dO V^T).
-  u32x4 kreg[NKS], vreg[NKS];
+  // This lane's key row of K (P wave) or V (dS wave): the B operand of
+  // S = Q K^T or dP = dO V^T.
+  u32x4 kv[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const int byte = my_k * ROWB + (ks * 16 + 8 * hh) * 2;
-    kreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(krs, byte, 0, 0);
-    if constexpr (!kDV) vreg[ks] = __builtin_amdgcn_raw_buffer_load_b128(vrs, byte, 0, 0);
-  }
+  for (int ks = 0; ks < NKS; ++ks)
+    kv[ks] = __builtin_amdgcn_raw_buffer_load_b128(kvrs, my_k * ROWB + (ks * 16 + 8 * hh) * 2, 0, 0);
 
   BlockAddr<ROWB> qa;
   qa.init(lane);
-  BlockLoader<ROWB> ld;
+  BlockLoader<ROWB, kKVWaves> ld;
   ld.init(wave, lane);
 
   // Query blocks that can see a key of this tile: all, or (causal) from the
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
   const int qb_begin = CAUSAL ? (k0 / kBS) : 0;
   const int nblk = (N - qb_begin * kBS + kBS - 1) / kBS;
 
-  f32x16 acc[NDT];  // dV^T (PART 1) or dK^T (PART 2)
+  f32x16 acc[NDT];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
 
@@ -460,66 +474,86 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
   store_lse(lse_lds0);
   bwd_barrier();
 
+  uint8_t* const pex = p_lds[grp];
   auto step = [&](int j, const uint8_t* qb, const uint8_t* db, const float* lb, const float* dlb,
                   uint8_t* qn, uint8_t* dn, float* ln, float* dln) __attribute__((always_inline)) {
     const int qrow0 = (qb_begin + j) * kBS;  // first query of this block
     ld.load(qrs, qn, qrow0 + kBS, N);
     ld.load(dors, dn, qrow0 + kBS, N);
     load_ld(dln, qrow0 + kBS);
-    f32x16 s[2], dp[2];
+    // S (P wave) or dP (dS wave), queries as rows, this lane's key as column.
+    const uint8_t* ab = pw ? qb : db;
+    f32x16 x[2];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      s[t2] = f32x16{};
-      dp[t2] = f32x16{};
-    }
+    for (int t2 = 0; t2 < 2; ++t2) x[t2] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        s[t2] = mfma16<DT>(row_operand<ROWB>(qb, qa, t2, ks), kreg[ks], s[t2]);
-        if constexpr (!kDV)
-          dp[t2] = mfma16<DT>(row_operand<ROWB>(db, qa, t2, ks), vreg[ks], dp[t2]);
-      }
-    mfma_read_pipeline<(kDV ? 2 : 4) * NKS, 1, 4>();
+      for (int t2 = 0; t2 < 2; ++t2)
+        x[t2] = mfma16<DT>(row_operand<ROWB>(ab, qa, t2, ks), kv[ks], x[t2]);
+    mfma_read_pipeline<2 * NKS, 1, 4>();
     __builtin_amdgcn_sched_barrier(0);
-    // P = exp2(cs s - lse log2 e), dS = P (dP - D); masked pairs give 0.
-    // w holds P (PART 1) or dS (PART 2) as pairs of the input type.
+    // w: P (P wave) or dS (dS wave) as pairs of the input type.  Elements
+    // 4 g .. 4 g + 3 of tile t2 are query rows t2*32 + 8 g + 4 hh .. +3, whose
+    // LSE log2 e (and D) are four consecutive floats; they go to k-step g / 2,
+    // dwords 2 (g % 2), +1.
     uint32_t w[2][2][4];
-    // Four accumulator rows at a time: elements 4 g .. 4 g + 3 of tile t2 are
-    // query rows t2*32 + 8 g + 4 hh .. +3, whose LSE log2 e (and D) are four
-    // consecutive floats.  Only a block reaching past N or below the tile's
-    // last key needs the mask (a uniform branch; exp2 of a masked score is
-    // replaced, never used).
-    const bool edge = qrow0 + kBS > N || (CAUSAL && qrow0 < k0 + kBT);
+    if (pw) {
+      // P = exp2(cs s - lse log2 e); masked pairs give 0.  Only a block
+      // reaching past N or below the tile's last key needs the mask (a
+      // uniform branch; exp2 of a masked score is replaced, never used).
+      const bool edge = qrow0 + kBS > N || (CAUSAL && qrow0 < k0 + kBT);
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lb + t2 * 32 + 8 * g + 4 * hh);
-        float pt[4];
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lb + t2 * 32 + 8 * g + 4 * hh);
+          float pt[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pt[i] = __builtin_amdgcn_exp2f(fmaf(s[t2][4 * g + i], cs, -lse4[i]));
-        if (edge) {
+          for (int i = 0; i < 4; ++i)
+            pt[i] = __builtin_amdgcn_exp2f(fmaf(x[t2][4 * g + i], cs, -lse4[i]));
+          if (edge) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int qi = qrow0 + t2 * 32 + 8 * g + 4 * hh + i;
-            bool keep = qi < N;
-            if constexpr (CAUSAL) keep = keep && qi >= my_k;
-            pt[i] = keep ? pt[i] : 0.0f;
+            for (int i = 0; i < 4; ++i) {
+              const int qi = qrow0 + t2 * 32 + 8 * g + 4 * hh + i;
+              bool keep = qi < N;
+              if constexpr (CAUSAL) keep = keep && qi >= my_k;
+              pt[i] = keep ? pt[i] : 0.0f;
+            }
           }
+          w[t2][g / 2][2 * (g % 2)] = pack2<DT>(pt[0], pt[1]);
+          w[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(pt[2], pt[3]);
         }
-        if constexpr (!kDV) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + t2 * 32 + 8 * g + 4 * hh);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pt[i] *= dp[t2][4 * g + i] - d4[i];
-        }
-        // elements 4 g .. 4 g + 3 go to k-step g / 2, dwords 2 (g % 2), +1
-        w[t2][g / 2][2 * (g % 2)] = pack2<DT>(pt[0], pt[1]);
-        w[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(pt[2], pt[3]);
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(pex + (c * kWave + lane) * 16) =
+            u32x4{w[c / 2][c % 2][0], w[c / 2][c % 2][1], w[c / 2][c % 2][2], w[c / 2][c % 2][3]};
+    }
+    lds_barrier();  // P is in LDS; the next block's loads stay in flight
+    if (!pw) {
+      // dS = P (dP - D) from the P wave's P, which is 0 at every masked pair.
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 pv = *reinterpret_cast<const u32x4*>(pex + (c * kWave + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[c / 2][c % 2][e] = pv[e];
       }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + t2 * 32 + 8 * g + 4 * hh);
+          float ds[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ds[i] = elem<DT>(w[t2][g / 2][2 * (g % 2) + i / 2], i % 2) * (x[t2][4 * g + i] - d4[i]);
+          w[t2][g / 2][2 * (g % 2)] = pack2<DT>(ds[0], ds[1]);
+          w[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(ds[2], ds[3]);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P, or dK^T += Q^T dS.
+    const uint8_t* tb = pw ? db : qb;
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -527,7 +561,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
 #pragma unroll
         for (int t = 0; t < NDT; ++t) {
           const u32x4 b = {w[t2][sg][0], w[t2][sg][1], w[t2][sg][2], w[t2][sg][3]};
-          acc[t] = mfma16<DT>(tr_operand<ROWB>(kDV ? db : qb, qa, t, 2 * t2 + sg), b, acc[t]);
+          acc[t] = mfma16<DT>(tr_operand<ROWB>(tb, qa, t, 2 * t2 + sg), b, acc[t]);
         }
     mfma_read_pipeline<4 * NDT, 2, 4>();
     store_lse(ln);  // the next block's LSE; ln was last read in the previous step
@@ -538,12 +572,14 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dkdv_kernel(BwdParams p
     step(j + 1, q_lds1, do_lds1, lse_lds1, d_lds1, q_lds0, do_lds0, lse_lds0, d_lds0);
   }
 
-  // As in the dQ kernel: the Q and dO stages are free after the loop.
+  // The Q and dO stages are free after the loop: dV leaves through them
+  // first, then dK.
   static_assert(kBwdWaves == 4 && BLK == kRW * D * 4, "one 32 x D fp32 block per stage");
-  uint8_t* sbuf = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? do_lds0 : do_lds1;
-  const int kw0 = k0 + wave * kRW;
-  store_rows_f32<D>(acc, kDV ? 1.0f : p.scale, sbuf, (kDV ? p.dv : p.dk) + head_off + (int64_t)kw0 * D,
-                    N - kw0, lane);
+  uint8_t* sbuf = grp == 0 ? q_lds0 : grp == 1 ? q_lds1 : grp == 2 ? do_lds0 : do_lds1;
+  const int kw0 = k0 + grp * kRW;
+  if (pw) store_rows_f32<D>(acc, 1.0f, sbuf, p.dv + head_off + (int64_t)kw0 * D, N - kw0, lane);
+  lds_barrier();
+  if (!pw) store_rows_f32<D>(acc, p.scale, sbuf, p.dk + head_off + (int64_t)kw0 * D, N - kw0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -562,11 +598,8 @@ int launch_bwd_t(BwdParams prm, hipStream_t stream) {
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<DT, D, CAUSAL>),
                                  grid, dim3(kBwdThreads), args, 0, stream);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL, 1>),
-                      grid, dim3(kBwdThreads), args, 0, stream);
-  if (e != hipSuccess) return FA_ERR_LAUNCH;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL, 2>),
-                      grid, dim3(kBwdThreads), args, 0, stream);
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL>), grid,
+                      dim3(kKVThreads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
