@@ -33,6 +33,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_mi355x.h"
 
@@ -394,18 +396,18 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
   constexpr int NDT = D / 32;
   constexpr int BLK = kBS * ROWB;
   constexpr int PBLK = kRW * kBS * 2;  // one group's P block in the input type
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds0[BLK];
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds1[BLK];
-  __shared__ __attribute__((aligned(16))) uint8_t do_lds0[BLK];
-  __shared__ __attribute__((aligned(16))) uint8_t do_lds1[BLK];
-  // LSE and D of the block's 64 queries.
-  __shared__ __attribute__((aligned(16))) float lse_lds0[kBS];
-  __shared__ __attribute__((aligned(16))) float lse_lds1[kBS];
-  __shared__ __attribute__((aligned(16))) float d_lds0[kBS];
-  __shared__ __attribute__((aligned(16))) float d_lds1[kBS];
+  // The P waves run one query block ahead of the dS waves: in step j a P
+  // wave computes P of block j + 1 (from Q_{j+1}) and dV of block j, its dS
+  // wave dS and dK of block j (from P_j, dO_j, Q_j), while Q_{j+2} and
+  // dO_{j+1} stream in -- three Q stages, two dO stages, one barrier a step.
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[3][BLK];
+  __shared__ __attribute__((aligned(16))) uint8_t do_lds[2][BLK];
+  // LSE (times log2 e) and D of a block's 64 queries.
+  __shared__ __attribute__((aligned(16))) float lse_lds[2][kBS];
+  __shared__ __attribute__((aligned(16))) float d_lds[2][kBS];
   // P of each key group, from its P wave to its dS wave: lane l's 16 dwords
   // as four 16-byte pieces at (c * 64 + l) * 16, c = 0 .. 3.
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[kBwdWaves][PBLK];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][kBwdWaves][PBLK];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -450,6 +452,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
   // block holding query k0 on.
   const int qb_begin = CAUSAL ? (k0 / kBS) : 0;
   const int nblk = (N - qb_begin * kBS + kBS - 1) / kBS;
+  auto row0_of = [&](int j) { return (qb_begin + j) * kBS; };
 
   f32x16 acc[NDT];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
@@ -459,30 +462,28 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
   // (wave 1); LSE passes through wave 0's registers to be stored already
   // multiplied by log2 e, once per row instead of once per score.
   float lse_next = 0.0f;
-  auto load_ld = [&](float* d_dst, int row0) __attribute__((always_inline)) {
+  auto load_lse = [&](int row0) __attribute__((always_inline)) {
     const int off = (row0 < N ? row0 : N) * 4 + lane * 4;  // past N: zeros
     if (wave == 0) lse_next = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, off, 0, 0));
-    if (wave == 1) buffer_to_lds4(drs, d_dst, off);
   };
   auto store_lse = [&](float* lse_dst) __attribute__((always_inline)) {
     if (wave == 0) lse_dst[lane] = lse_next * kLog2e;
   };
+  auto load_d = [&](float* d_dst, int row0) __attribute__((always_inline)) {
+    const int off = (row0 < N ? row0 : N) * 4 + lane * 4;
+    if (wave == 1) buffer_to_lds4(drs, d_dst, off);
+  };
 
-  ld.load(qrs, q_lds0, qb_begin * kBS, N);
-  ld.load(dors, do_lds0, qb_begin * kBS, N);
-  load_ld(d_lds0, qb_begin * kBS);
-  store_lse(lse_lds0);
-  bwd_barrier();
-
-  uint8_t* const pex = p_lds[grp];
-  auto step = [&](int j, const uint8_t* qb, const uint8_t* db, const float* lb, const float* dlb,
-                  uint8_t* qn, uint8_t* dn, float* ln, float* dln) __attribute__((always_inline)) {
-    const int qrow0 = (qb_begin + j) * kBS;  // first query of this block
-    ld.load(qrs, qn, qrow0 + kBS, N);
-    ld.load(dors, dn, qrow0 + kBS, N);
-    load_ld(dln, qrow0 + kBS);
-    // S (P wave) or dP (dS wave), queries as rows, this lane's key as column.
-    const uint8_t* ab = pw ? qb : db;
+  // P of block j (P wave): S = Q K^T from Q block qb, exp2 against the
+  // block's LSE, masked pairs 0, as pairs of the input type in w.  Elements
+  // 4 g .. 4 g + 3 of tile t2 are query rows t2*32 + 8 g + 4 hh .. +3, whose
+  // LSE log2 e (and D) are four consecutive floats; they go to k-step g / 2,
+  // dwords 2 (g % 2), +1.  The P goes to LDS at px, for the dS wave and for
+  // the P wave's own dV product a step later.
+  auto p_block = [&](int j, const uint8_t* qb, const float* lb, uint8_t* px)
+      __attribute__((always_inline)) {
+    const int qrow0 = row0_of(j);
+    uint32_t w[2][2][4];
     f32x16 x[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) x[t2] = f32x16{};
@@ -490,70 +491,52 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
-        x[t2] = mfma16<DT>(row_operand<ROWB>(ab, qa, t2, ks), kv[ks], x[t2]);
+        x[t2] = mfma16<DT>(row_operand<ROWB>(qb, qa, t2, ks), kv[ks], x[t2]);
     mfma_read_pipeline<2 * NKS, 1, 4>();
     __builtin_amdgcn_sched_barrier(0);
-    // w: P (P wave) or dS (dS wave) as pairs of the input type.  Elements
-    // 4 g .. 4 g + 3 of tile t2 are query rows t2*32 + 8 g + 4 hh .. +3, whose
-    // LSE log2 e (and D) are four consecutive floats; they go to k-step g / 2,
-    // dwords 2 (g % 2), +1.
-    uint32_t w[2][2][4];
-    if (pw) {
-      // P = exp2(cs s - lse log2 e); masked pairs give 0.  Only a block
-      // reaching past N or below the tile's last key needs the mask (a
-      // uniform branch; exp2 of a masked score is replaced, never used).
-      const bool edge = qrow0 + kBS > N || (CAUSAL && qrow0 < k0 + kBT);
+    // Only a block reaching past N or below the tile's last key needs the
+    // mask (a uniform branch; exp2 of a masked score is replaced, never used).
+    const bool edge = qrow0 + kBS > N || (CAUSAL && qrow0 < k0 + kBT);
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lb + t2 * 32 + 8 * g + 4 * hh);
-          float pt[4];
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lb + t2 * 32 + 8 * g + 4 * hh);
+        float pt[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pt[i] = __builtin_amdgcn_exp2f(fmaf(x[t2][4 * g + i], cs, -lse4[i]));
-          if (edge) {
+        for (int i = 0; i < 4; ++i)
+          pt[i] = __builtin_amdgcn_exp2f(fmaf(x[t2][4 * g + i], cs, -lse4[i]));
+        if (edge) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int qi = qrow0 + t2 * 32 + 8 * g + 4 * hh + i;
-              bool keep = qi < N;
-              if constexpr (CAUSAL) keep = keep && qi >= my_k;
-              pt[i] = keep ? pt[i] : 0.0f;
-            }
+          for (int i = 0; i < 4; ++i) {
+            const int qi = qrow0 + t2 * 32 + 8 * g + 4 * hh + i;
+            bool keep = qi < N;
+            if constexpr (CAUSAL) keep = keep && qi >= my_k;
+            pt[i] = keep ? pt[i] : 0.0f;
           }
-          w[t2][g / 2][2 * (g % 2)] = pack2<DT>(pt[0], pt[1]);
-          w[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(pt[2], pt[3]);
         }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<u32x4*>(pex + (c * kWave + lane) * 16) =
-            u32x4{w[c / 2][c % 2][0], w[c / 2][c % 2][1], w[c / 2][c % 2][2], w[c / 2][c % 2][3]};
-    }
-    lds_barrier();  // P is in LDS; the next block's loads stay in flight
-    if (!pw) {
-      // dS = P (dP - D) from the P wave's P, which is 0 at every masked pair.
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 pv = *reinterpret_cast<const u32x4*>(pex + (c * kWave + lane) * 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[c / 2][c % 2][e] = pv[e];
+        w[t2][g / 2][2 * (g % 2)] = pack2<DT>(pt[0], pt[1]);
+        w[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(pt[2], pt[3]);
       }
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<u32x4*>(px + (c * kWave + lane) * 16) =
+          u32x4{w[c / 2][c % 2][0], w[c / 2][c % 2][1], w[c / 2][c % 2][2], w[c / 2][c % 2][3]};
+  };
+
+  // The 16 dwords of a P block that this lane wrote (or its partner wave's
+  // lane wrote) at px.
+  auto read_p = [&](const uint8_t* px, uint32_t (&w)[2][2][4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + t2 * 32 + 8 * g + 4 * hh);
-          float ds[4];
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 pv = *reinterpret_cast<const u32x4*>(px + (c * kWave + lane) * 16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ds[i] = elem<DT>(w[t2][g / 2][2 * (g % 2) + i / 2], i % 2) * (x[t2][4 * g + i] - d4[i]);
-          w[t2][g / 2][2 * (g % 2)] = pack2<DT>(ds[0], ds[1]);
-          w[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(ds[2], ds[3]);
-        }
+      for (int e = 0; e < 4; ++e) w[c / 2][c % 2][e] = pv[e];
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P, or dK^T += Q^T dS.
-    const uint8_t* tb = pw ? db : qb;
+  };
+
+  // acc += (block tb)^T w: dV^T += dO^T P or dK^T += Q^T dS.
+  auto second = [&](const uint8_t* tb, const uint32_t (&w)[2][2][4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -564,18 +547,88 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
           acc[t] = mfma16<DT>(tr_operand<ROWB>(tb, qa, t, 2 * t2 + sg), b, acc[t]);
         }
     mfma_read_pipeline<4 * NDT, 2, 4>();
-    store_lse(ln);  // the next block's LSE; ln was last read in the previous step
+  };
+
+  ld.load(qrs, q_lds[0], row0_of(0), N);
+  ld.load(qrs, q_lds[1], row0_of(1), N);
+  ld.load(dors, do_lds[0], row0_of(0), N);
+  load_d(d_lds[0], row0_of(0));
+  load_lse(row0_of(0));
+  store_lse(lse_lds[0]);
+  load_lse(row0_of(1));
+  store_lse(lse_lds[1]);
+  bwd_barrier();
+  if (pw) p_block(0, q_lds[0], lse_lds[0], p_lds[0][grp]);
+  bwd_barrier();
+
+  // Step j; stage indices are j mod 3 (Q) and j mod 2 (the rest), fixed per
+  // unrolled copy U = j mod 6.
+  auto step = [&](int j, auto uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(uc)::value;
+    constexpr int Q0 = U % 3, Q1 = (U + 1) % 3, Q2 = (U + 2) % 3, S0 = U % 2, S1 = (U + 1) % 2;
+    ld.load(qrs, q_lds[Q2], row0_of(j + 2), N);
+    ld.load(dors, do_lds[S1], row0_of(j + 1), N);
+    load_d(d_lds[S1], row0_of(j + 1));
+    load_lse(row0_of(j + 2));
+    if (pw) {
+      // dV^T += dO_j^T P_j, P_j read back from LDS; then P of block j + 1.
+      uint32_t w[2][2][4];
+      read_p(p_lds[S0][grp], w);
+      second(do_lds[S0], w);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < nblk) p_block(j + 1, q_lds[Q1], lse_lds[S1], p_lds[S1][grp]);
+    } else {
+      // dP = dO V^T, then dS = P (dP - D) from the P wave's P, which is 0 at
+      // every masked pair.
+      f32x16 x[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) x[t2] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+          x[t2] = mfma16<DT>(row_operand<ROWB>(do_lds[S0], qa, t2, ks), kv[ks], x[t2]);
+      mfma_read_pipeline<2 * NKS, 1, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t ds[2][2][4];
+      read_p(p_lds[S0][grp], ds);
+      const float* dlb = d_lds[S0];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + t2 * 32 + 8 * g + 4 * hh);
+          float v4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v4[i] = elem<DT>(ds[t2][g / 2][2 * (g % 2) + i / 2], i % 2) * (x[t2][4 * g + i] - d4[i]);
+          ds[t2][g / 2][2 * (g % 2)] = pack2<DT>(v4[0], v4[1]);
+          ds[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(v4[2], v4[3]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      second(q_lds[Q0], ds);
+    }
+    store_lse(lse_lds[S0]);  // LSE of block j + 2; lse_lds[S0] held block j's, used in step j - 1
     bwd_barrier();
   };
-  for (int j = 0; j < nblk; j += 2) {
-    step(j, q_lds0, do_lds0, lse_lds0, d_lds0, q_lds1, do_lds1, lse_lds1, d_lds1);
-    step(j + 1, q_lds1, do_lds1, lse_lds1, d_lds1, q_lds0, do_lds0, lse_lds0, d_lds0);
+  for (int j = 0; j < nblk; j += 6) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 >= nblk) break;
+    step(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 >= nblk) break;
+    step(j + 2, std::integral_constant<int, 2>{});
+    if (j + 3 >= nblk) break;
+    step(j + 3, std::integral_constant<int, 3>{});
+    if (j + 4 >= nblk) break;
+    step(j + 4, std::integral_constant<int, 4>{});
+    if (j + 5 >= nblk) break;
+    step(j + 5, std::integral_constant<int, 5>{});
   }
 
-  // The Q and dO stages are free after the loop: dV leaves through them
-  // first, then dK.
+  // Every stage is free after the loop's last barrier: dV leaves through
+  // four of them first, then dK.
   static_assert(kBwdWaves == 4 && BLK == kRW * D * 4, "one 32 x D fp32 block per stage");
-  uint8_t* sbuf = grp == 0 ? q_lds0 : grp == 1 ? q_lds1 : grp == 2 ? do_lds0 : do_lds1;
+  uint8_t* sbuf = grp < 3 ? q_lds[grp] : do_lds[0];
   const int kw0 = k0 + grp * kRW;
   if (pw) store_rows_f32<D>(acc, 1.0f, sbuf, p.dv + head_off + (int64_t)kw0 * D, N - kw0, lane);
   lds_barrier();
