@@ -222,8 +222,10 @@ int fa_fwd_fp8_pv_kvsplit(const void* q, const void* k, const void* v,
  * same q, k, v, scale and causal (fa_fwd's, or any consistent pair).  All
  * pointers are device pointers, 16-byte aligned, none NULL when B*H*N > 0;
  * the library allocates nothing (delta is the caller's workspace and an
- * output).  dtype FP8 returns FA_ERR_DTYPE.  Three kernels are enqueued on
- * the stream (dQ with delta, then dV, then dK).  Returns FA_OK or a negative fa_status.
+ * output).  dtype FP8 returns FA_ERR_DTYPE.  Two kernels are enqueued on
+ * the stream: dQ with delta, then dK and dV together.  P and dS enter the
+ * products dV, dQ, dK rounded to dtype (dK's dS formed from that rounded P);
+ * everything else accumulates in fp32.  Returns FA_OK or a negative fa_status.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, float* dq, float* dk, float* dv,
