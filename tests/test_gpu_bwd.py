@@ -92,6 +92,26 @@ def test_bwd_small(dtype, d, causal, N):
     assert torch.allclose(delta.cpu().double(), want, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nq", range(1, 8))
+def test_bwd_every_block_count(d, nq):
+    # The dK/dV loop is unrolled six times and may leave after any copy:
+    # query block counts 1 .. 7 (N = 64 nq - 1, the last block ragged) reach
+    # every exit and the wrap back to the first copy.
+    N = 64 * nq - 1
+    inp = inputs.draw_bwd(1, 2, N, d, "fp16" if nq % 2 else "bf16", False, seed=3200 + nq + d)
+    dq, dk, dv, _, _ = run_bwd(inp)
+    check_grads(inp, (dq, dk, dv))
+
+
+def test_bwd_causal_tiles_of_every_length():
+    # Causal, N = 827: the 128-key tiles start at query blocks 0, 2, .., 12
+    # and run 13, 11, 9, 7, 5, 3, 1 blocks.
+    inp = inputs.draw_bwd(1, 2, 827, 128, "bf16", True, seed=3300)
+    dq, dk, dv, _, _ = run_bwd(inp)
+    check_grads(inp, (dq, dk, dv))
+
+
 @pytest.mark.parametrize("dtype,causal", [("fp16", False), ("bf16", True)])
 def test_bwd_medium_sampled_heads(dtype, causal):
     inp = inputs.draw_bwd(1, 8, 1500, 128, dtype, causal, seed=3100)
