@@ -21,10 +21,12 @@
 //     dK^T += Q^T dS; dO^T / Q^T are read transposed from the row-major
 //     dO / Q blocks.
 // Blocks stream global -> LDS (buffer_load ... lds, XOR-swizzled 16-byte
-// chunks) into two buffers, one barrier per block; the loops are unrolled by
-// two so each buffer is its own LDS array.  Rows past N read as zeros and are
-// masked, as are causal pairs (key j > query i); a loop runs to an even block
-// count, the extra block fully masked.  P and dS enter the second products
+// chunks), one barrier per block: the dQ kernel double-buffers K and V and
+// unrolls its loop by two (running to an even block count, the extra block
+// fully masked); the dK/dV kernel keeps three Q stages and two dO stages and
+// unrolls by six, leaving after the last block.  Every stage index is thus a
+// constant.  Rows past N read as zeros and are masked, as are causal pairs
+// (key j > query i).  P and dS enter the second products
 // in the input type (fp16 or bf16, round to nearest even); the dK kernel's dS
 // is formed from that rounded P, the dQ kernel's from P in fp32.  All
 // accumulation is fp32 and the gradients are stored as fp32.
