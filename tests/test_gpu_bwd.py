@@ -138,3 +138,32 @@ def test_bwd_rejects_fp8():
                     x.data_ptr(), f.data_ptr(), f.data_ptr(), f.data_ptr(), l.data_ptr(),
                     1, 1, 64, 64, 0.125, 0, 2, None)
     assert binding.status_string(st) == "unknown dtype"
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_bwd_no_writes_outside_outputs(d, causal):
+    # dq, dk, dv and delta carved out of larger buffers holding a sentinel:
+    # the row stores of a ragged last tile (N = 333: key groups of 32 rows
+    # end at 320 and 352) must leave the guard bands alone.
+    inp = inputs.draw_bwd(1, 3, 333, d, "fp16", causal, seed=3400 + d)
+    q, k, v, _ = binding.to_device(inp)
+    do = _up(inp.do, inp.dtype)
+    o, lse = binding.fwd(q, k, v, causal=causal, scale=inp.scale)
+    B, H, N = inp.B, inp.H, inp.N
+    G = 4096  # guard floats on each side, a multiple of 4: outputs stay 16-byte aligned
+    n, nr = B * H * N * d, B * H * N
+    bufs = [torch.full((n + 2 * G,), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+    dbuf = torch.full((nr + 2 * G,), 7.0, dtype=torch.float32, device="cuda")
+    dq, dk, dv = (b[G:G + n] for b in bufs)
+    delta = dbuf[G:G + nr]
+    lib = binding.load_library()
+    st = lib.fa_bwd(binding._ptr(q), binding._ptr(k), binding._ptr(v), binding._ptr(o),
+                    binding._ptr(lse), binding._ptr(do), binding._ptr(dq), binding._ptr(dk),
+                    binding._ptr(dv), binding._ptr(delta), B, H, N, d, inp.scale, int(causal),
+                    binding._TORCH_DTYPE_CODE[q.dtype], torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    for b in bufs + [dbuf]:
+        m = b.numel() - 2 * G
+        assert torch.all(b[:G] == 7.0) and torch.all(b[G + m:] == 7.0)
+    check_grads(inp, tuple(t.view(B, H, N, d) for t in (dq, dk, dv)))
