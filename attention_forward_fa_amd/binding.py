@@ -330,9 +330,13 @@ def fwd_fp8_pv_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, min_ke
 
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
-        dout: torch.Tensor, causal: bool = False, scale: Optional[float] = None):
+        dout: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+        dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+        dv: Optional[torch.Tensor] = None, delta: Optional[torch.Tensor] = None):
     """dQ, dK, dV (fp32 [B, H, N, d]) and delta = rowsum(dO * O) (fp32 [B, H, N])
-    for fp16 / bf16 q, k, v, dout, the forward's o (fp16) and lse."""
+    for fp16 / bf16 q, k, v, dout, the forward's o (fp16) and lse.  Output
+    buffers may be passed in (contiguous, on q's device), else they are
+    allocated."""
     _validate(q, k, v)
     if q.dtype not in (torch.float16, torch.bfloat16):
         raise TypeError("the backward pass takes float16 or bfloat16 q, k, v")
@@ -346,9 +350,18 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     for t in (dout, o, lse):
         if t.device != q.device:
             raise ValueError("all tensors must be on one device")
-    dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-                  for _ in range(3))
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+
+    def out_buf(t, shape):
+        if t is None:
+            return torch.empty(shape, dtype=torch.float32, device=q.device)
+        if (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32
+                or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"gradient outputs must be contiguous float32 {tuple(shape)} "
+                             "tensors on q's device")
+        return t
+
+    dq, dk, dv = (out_buf(t, (B, H, N, d)) for t in (dq, dk, dv))
+    delta = out_buf(delta, (B, H, N))
     scale = _default_scale(d) if scale is None else float(scale)
     lib = load_library()
     with torch.cuda.device(q.device):

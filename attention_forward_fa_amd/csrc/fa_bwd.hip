@@ -62,6 +62,7 @@ struct BwdParams {
   int N;
   int n_tiles;
   int bh;
+  int n_xcd;  // XCDs of the device (workgroup -> XCD mapping of tile_of)
   float scale;
 };
 
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
   const int lr = lane & 31, hh = lane >> 5;
 
   int bh, qt;
-  tile_of(blockIdx.x, p.bh, p.n_tiles, CAUSAL, bh, qt);
+  tile_of(blockIdx.x, p.bh, p.n_tiles, CAUSAL, p.n_xcd, bh, qt);
   const int N = p.N;
   const int64_t head_off = (int64_t)bh * N * D;
   const int head_bytes = N * ROWB;
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
   // Causal work shrinks with the key tile: tile_of hands out its heavy-first
   // order in reverse tile index, so turn it around.
   int bh, tt;
-  tile_of(blockIdx.x, p.bh, p.n_tiles, CAUSAL, bh, tt);
+  tile_of(blockIdx.x, p.bh, p.n_tiles, CAUSAL, p.n_xcd, bh, tt);
   const int kt = CAUSAL ? p.n_tiles - 1 - tt : tt;
   const int N = p.N;
   const int64_t head_off = (int64_t)bh * N * D;
@@ -701,6 +702,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   prm.N = (int)N;
   prm.n_tiles = 0;
   prm.bh = (int)(B * H);
+  prm.n_xcd = device_topology().xcds;
   prm.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return dtype == FA_DTYPE_BF16 ? launch_bwd_dt<FA_DTYPE_BF16>(prm, (int)d, causal, s)

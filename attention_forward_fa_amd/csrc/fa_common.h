@@ -7,6 +7,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa_mi355x.h"
 
 namespace {
@@ -104,20 +106,20 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, uint8
 }
 
 // Workgroup -> (head, query tile).  Workgroups are dispatched round-robin over
-// the 8 XCDs (workgroup w runs on XCD w % 8), and each XCD has its own L2.  When
-// the head count is a multiple of 8, XCD x gets heads x, x+8, x+16, ... so all
-// query tiles of a head, which re-read the same K and V, share one L2.  Within
-// an XCD, causal work goes longest tiles first (the last query tile of each of
-// its heads, then the one before, ...); non-causal work goes head by head.
-__device__ __forceinline__ void tile_of(int w, int n_heads, int n_tiles, bool causal, int& bh,
-                                        int& qt) {
-  constexpr int kXcd = 8;
+// the device's n_xcd XCDs (workgroup w runs on XCD w % n_xcd), and each XCD
+// has its own L2.  When the head count is a multiple of n_xcd, XCD x gets
+// heads x, x + n_xcd, ... so all query tiles of a head, which re-read the
+// same K and V, share one L2.  Within an XCD, causal work goes longest tiles
+// first (the last query tile of each of its heads, then the one before, ...);
+// non-causal work goes head by head.
+__device__ __forceinline__ void tile_of(int w, int n_heads, int n_tiles, bool causal, int n_xcd,
+                                        int& bh, int& qt) {
   int head_slot, rank, heads_here, xcd = 0, stride = 1;
-  if (n_heads % kXcd == 0) {
-    xcd = w % kXcd;
-    w /= kXcd;
-    heads_here = n_heads / kXcd;
-    stride = kXcd;
+  if (n_xcd > 1 && n_heads % n_xcd == 0) {
+    xcd = w % n_xcd;
+    w /= n_xcd;
+    heads_here = n_heads / n_xcd;
+    stride = n_xcd;
   } else {
     heads_here = n_heads;
   }
@@ -130,6 +132,43 @@ __device__ __forceinline__ void tile_of(int w, int n_heads, int n_tiles, bool ca
     qt = w % n_tiles;
   }
   bh = head_slot * stride + xcd;
+}
+
+// Compute units and XCDs of the current device, read from the runtime once
+// per device and cached; launch shapes, the workgroup -> XCD mapping and the
+// key-range split plan depend on them.  If the runtime cannot tell, a whole
+// MI355X is assumed (256 CUs in 8 XCDs).  Called only after a call's
+// arguments have been validated.
+struct Topology {
+  int cus;
+  int xcds;
+};
+
+inline Topology device_topology() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // cus << 8 | xcds; 0: not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return {256, 8};
+  }
+  if (dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0) return {c >> 8, c & 255};
+  }
+  int cus = 0, xcds = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0 || cus >= (1 << 20)) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+      xcds <= 0 || xcds > 255) {
+    (void)hipGetLastError();
+    xcds = cus == 256 ? 8 : 1;
+  }
+  if (dev < kMaxDevices) cache[dev].store(cus << 8 | xcds, std::memory_order_relaxed);
+  return {cus, xcds};
 }
 
 }  // namespace

@@ -93,7 +93,6 @@ struct Shape {
   static constexpr int br = kQW * waves;  // query rows per workgroup
 };
 constexpr int kMinBR = kQW * 4;           // smallest query tile of any kernel
-constexpr int kCUs = 256;                 // compute units of an MI355X
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma_qk(const QKOperand<DT>& a, const QKOperand<DT>& b,
@@ -210,6 +209,7 @@ struct Params {
   int bh;      // B*H
   int layout;  // FA_LAYOUT_BHND or FA_LAYOUT_BNHD (q, k, v and o alike)
   int qt_base; // first query tile of this launch (n_qtiles tiles from there)
+  int n_xcd;   // XCDs of the device (workgroup -> XCD mapping of tile_of)
   float scale;
   // Key-range split (split_g > 0): workgroup w takes head w % bh and the
   // (w / bh)-th chunk of that head, longest tiles first.  A tile's key range,
@@ -315,7 +315,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     chunk = u;
     n_chunks = (n_groups + g - 1) / g;
   } else {
-    tile_of(blockIdx.x, p.bh, p.n_qtiles, CAUSAL, bh, qt);
+    tile_of(blockIdx.x, p.bh, p.n_qtiles, CAUSAL, p.n_xcd, bh, qt);
     qt += p.qt_base;
   }
   const int N = p.N;
@@ -1087,13 +1087,13 @@ int launch_all(const Params& prm, hipStream_t stream) {
 }
 
 template <int DT, int D, bool CAUSAL>
-int launch_t(const Params& prm, hipStream_t stream) {
+int launch_t(const Params& prm, int cus, hipStream_t stream) {
   constexpr int W = default_waves<DT, D>();
   const int64_t wgs8 = (int64_t)prm.bh * ((prm.N + Shape<8>::br - 1) / Shape<8>::br);
   if constexpr (W == 8) {
     // With 256-row tiles filling at most half the CUs, 128-row tiles on all of
     // them finish sooner although one wave per SIMD runs slower than two.
-    if (2 * wgs8 <= kCUs) return launch_all<DT, D, CAUSAL, 4>(prm, stream);
+    if (2 * wgs8 <= cus) return launch_all<DT, D, CAUSAL, 4>(prm, stream);
   }
   if constexpr (D == 64 && DT != FA_DTYPE_FP8_E4M3 && !CAUSAL) {
     // Non-causal d = 64 with tiles of 16 or more key blocks: one 8-wave
@@ -1101,7 +1101,7 @@ int launch_t(const Params& prm, hipStream_t stream) {
     // (fp16 [4,16,1024,64] 26.0 -> 24.9 us, [2,16,4096,64] 178 -> 171 us); with
     // 8 blocks ([16,32,512,64] 53 -> 58 us) or causal tiles the three
     // co-resident 4-wave workgroups hide the per-tile cost better.
-    if (prm.N >= 1024 && 2 * wgs8 > kCUs) return launch_all<DT, D, CAUSAL, 8>(prm, stream);
+    if (prm.N >= 1024 && 2 * wgs8 > cus) return launch_all<DT, D, CAUSAL, 8>(prm, stream);
   }
   return launch_all<DT, D, CAUSAL, W>(prm, stream);
 }
@@ -1130,9 +1130,12 @@ int launch_pv8(const Params& prm, int64_t min_keys, hipStream_t stream) {
 }
 
 template <int DT>
-int launch_dt(const Params& prm, int d, int causal, hipStream_t stream) {
-  if (d == 64) return causal ? launch_t<DT, 64, true>(prm, stream) : launch_t<DT, 64, false>(prm, stream);
-  return causal ? launch_t<DT, 128, true>(prm, stream) : launch_t<DT, 128, false>(prm, stream);
+int launch_dt(const Params& prm, int d, int causal, int cus, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_t<DT, 64, true>(prm, cus, stream)
+                  : launch_t<DT, 64, false>(prm, cus, stream);
+  return causal ? launch_t<DT, 128, true>(prm, cus, stream)
+                : launch_t<DT, 128, false>(prm, cus, stream);
 }
 
 // Key-range split for grids that would leave CUs idle or hand the causal tail
@@ -1145,14 +1148,24 @@ int launch_dt(const Params& prm, int d, int causal, hipStream_t stream) {
 // group times (the half for a chunk's prologue and epilogue), and every chunk
 // of a split tile adds its partial O and LSE, written and read back once, at
 // an effective 5 TB/s.  A group takes 4 BR^2 d FLOP at the slot's share of
-// the kernel's measured throughput (about 1.0 PFLOP/s for fp16 / bf16, 1.3
-// for fp8, 0.6 of that at d = 64).  Unsplit, the time is the longest tile or
+// its CU's throughput (kSplitRatePerCU).  Unsplit, the time is the longest tile or
 // the work per slot, whichever is larger -- for an 8-wave grid small enough
 // to run on the 4-wave twin, with the twin's 128-row tiles (half a group row
 // each) at about 0.8 of the 8-wave rate.  The split is taken when estimated
 // at least 5 % faster (the estimate has erred on the slow side: shapes
 // estimated 5-15 % faster ran 5-9 % faster); grids with at least two tiles
 // per slot are left whole (the longest-first order balances them).
+// Forward throughput of one CU that the plan assumes, FLOP/s: the whole-grid
+// rates the kernels sustain on a 256-CU MI355X under its power limit, divided
+// by 256 -- fp16 / bf16 at d = 128 about 1.0 PFLOP/s, fp8 (P V in fp16) about
+// 1.3, both at about 0.6 of that at d = 64 (the kernel traces of the default
+// workload, the fp8 causal workload and the shapes listed in
+// profiles/fa_fwd_workloads_kernel_trace.md).  Only their ratio to the
+// partial-result traffic matters, and only roughly.
+constexpr double kSplitRatePerCU[2][2] = {  // [fp8][d == 128]
+    {0.6e15 / 256, 1.0e15 / 256},
+    {0.6 * 1.3e15 / 256, 1.3e15 / 256}};
+
 struct SplitPlan {
   int g = 0;     // chunk size in groups; 0: no split
   int cmax = 0;  // chunks of the longest tile
@@ -1162,10 +1175,11 @@ struct SplitPlan {
   int64_t ws_bytes = 0;
 };
 
-SplitPlan plan_split(int64_t BH, int64_t N, int64_t d, bool causal, int dtype) {
+SplitPlan plan_split(int64_t BH, int64_t N, int64_t d, bool causal, int dtype, int cus) {
   SplitPlan pl;
   const int br = (d == 128 && dtype != FA_DTYPE_FP8_E4M3) ? 256 : 128;  // default_waves * 32
-  const int64_t slots = (int64_t)kCUs * (br == 256 ? 1 : 2);
+  const int per_cu = br == 256 ? 1 : 2;  // resident workgroups per CU
+  const int64_t slots = (int64_t)cus * per_cu;
   const int64_t T = (N + br - 1) / br;
   pl.T = (int)T;
   pl.br = br;
@@ -1175,14 +1189,14 @@ SplitPlan plan_split(int64_t BH, int64_t N, int64_t d, bool causal, int dtype) {
     const int64_t full = T / g, rem = T % g;  // sum over t < T of ceil((t + 1) / g)
     return g * full * (full + 1) / 2 + rem * (full + 1);
   };
-  const double rate = (dtype == FA_DTYPE_FP8_E4M3 ? 1.3e15 : 1.0e15) * (d == 64 ? 0.6 : 1.0);
-  const double t_group = 4.0 * br * br * (double)d / (rate / (double)slots);  // seconds
+  const double rate = kSplitRatePerCU[dtype == FA_DTYPE_FP8_E4M3][d == 128];
+  const double t_group = 4.0 * br * br * (double)d / (rate / per_cu);  // seconds
   const double t_partial = 2.0 * br * (2.0 * d + 4.0) / 5e12;  // write + read of a chunk's partial, seconds
   const int64_t total = causal ? BH * T * (T + 1) / 2 : BH * T * T;
   double whole;
-  if (br == 256 && 2 * BH * T <= kCUs) {  // launch_t runs the 4-wave twin
+  if (br == 256 && 2 * BH * T <= cus) {  // launch_t runs the 4-wave twin
     const double longest = 0.5 * (double)T / 0.8;
-    whole = t_group * (causal ? fmax(longest, (double)total / (0.8 * kCUs)) : longest);
+    whole = t_group * (causal ? fmax(longest, (double)total / (0.8 * cus)) : longest);
   } else {
     whole = t_group * (causal ? fmax((double)T, (double)((total + slots - 1) / slots))
                               : (double)((BH * T + slots - 1) / slots) * (double)T);
@@ -1316,6 +1330,8 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   prm.split_cmax = 0;
   prm.ws_o = nullptr;
   prm.ws_lse = nullptr;
+  const Topology topo = device_topology();
+  prm.n_xcd = topo.xcds;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (split && split->g > 0 && dtype == FA_DTYPE_FP8_E4M3 && pv8_min_keys >= 0) {
     if (d == 64)
@@ -1339,9 +1355,9 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
                   : launch_pv8<128, false>(prm, pv8_min_keys, s);
   }
   switch (dtype) {
-    case FA_DTYPE_FP16: return launch_dt<FA_DTYPE_FP16>(prm, (int)d, causal, s);
-    case FA_DTYPE_BF16: return launch_dt<FA_DTYPE_BF16>(prm, (int)d, causal, s);
-    default: return launch_dt<FA_DTYPE_FP8_E4M3>(prm, (int)d, causal, s);
+    case FA_DTYPE_FP16: return launch_dt<FA_DTYPE_FP16>(prm, (int)d, causal, topo.cus, s);
+    case FA_DTYPE_BF16: return launch_dt<FA_DTYPE_BF16>(prm, (int)d, causal, topo.cus, s);
+    default: return launch_dt<FA_DTYPE_FP8_E4M3>(prm, (int)d, causal, topo.cus, s);
   }
 }
 
@@ -1416,7 +1432,7 @@ extern "C" int64_t fa_fwd_kvsplit_workspace(int64_t B, int64_t H, int64_t N, int
   const int st = check_problem(B, H, N, d, 1.0f, causal, dtype, FA_LAYOUT_BHND, &empty);
   if (st != FA_OK) return st;
   if (empty) return 0;
-  return plan_split(B * H, N, d, causal != 0, dtype).ws_bytes;
+  return plan_split(B * H, N, d, causal != 0, dtype, device_topology().cus).ws_bytes;
 }
 
 extern "C" int fa_fwd_kvsplit(const void* q, const void* k, const void* v, const float* descale_q,
@@ -1438,7 +1454,7 @@ extern "C" int fa_fwd_kvsplit(const void* q, const void* k, const void* v, const
   } else {
     descale_q = descale_k = descale_v = nullptr;
   }
-  const SplitPlan pl = plan_split(B * H, N, d, causal != 0, dtype);
+  const SplitPlan pl = plan_split(B * H, N, d, causal != 0, dtype, device_topology().cus);
   if (pl.g > 0) {
     if (!workspace) return FA_ERR_NULL;
     if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
@@ -1465,7 +1481,8 @@ extern "C" int fa_fwd_fp8_pv_kvsplit(const void* q, const void* k, const void* v
   if (given != 0 && given != 3) return FA_ERR_NULL;
   if (given == 3 && (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
     return FA_ERR_ALIGN;
-  const SplitPlan pl = plan_split(B * H, N, d, causal != 0, FA_DTYPE_FP8_E4M3);
+  const SplitPlan pl = plan_split(B * H, N, d, causal != 0, FA_DTYPE_FP8_E4M3,
+                                  device_topology().cus);
   if (pl.g > 0) {
     if (!workspace) return FA_ERR_NULL;
     if (!aligned(workspace, 256)) return FA_ERR_ALIGN;

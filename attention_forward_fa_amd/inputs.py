@@ -13,7 +13,9 @@ Recipe (the workloads of the five attention configurations):
   * fp8 (OCP e4m3fn): per (b, h) slice, ``amax = max |x|`` over N x d,
     ``s = amax / 448`` in float32 (``s = 1`` for an all-zero slice), codes =
     RNE(clamp(x / s, -448, 448)); ``s`` is the dequantization scale
-    ("descale") handed to both sides.
+    ("descale") handed to both sides.  With key tiles of T rows (kv_tile),
+    K and V are quantized the same way per (b, h, tile of T consecutive rows)
+    instead, one descale per tile; Q stays per (b, h).
   * scale = 1/sqrt(d) rounded to float32, unless the caller fixes another.
 
 Arrays are returned as raw storage bits (uint16 for fp16/bf16, uint8 for fp8)
@@ -59,6 +61,9 @@ class AttnInputs:
     descale_v: Optional[np.ndarray] = None
     seed: Optional[int] = None
     do: Optional[np.ndarray] = None  # dL/dO bits (backward inputs), same storage type
+    # fp8 only: K and V quantized per tile of kv_tile rows; descale_k and
+    # descale_v are then [B*H*ceil(N/kv_tile)], tile t of head f at f*nt + t.
+    kv_tile: Optional[int] = None
 
     @property
     def shape(self):
@@ -66,7 +71,8 @@ class AttnInputs:
 
     def describe(self) -> str:
         return (f"B={self.B} H={self.H} N={self.N} d={self.d} dtype={self.dtype} "
-                f"causal={int(self.causal)} seed={self.seed}")
+                f"causal={int(self.causal)} seed={self.seed}"
+                + (f" kv_tile={self.kv_tile}" if self.kv_tile else ""))
 
 
 def default_scale(d: int) -> float:
@@ -78,21 +84,32 @@ def _bits(t: torch.Tensor, dtype: str) -> np.ndarray:
     return t.contiguous().view(_BITS_VIEW[dtype]).numpy().view(_NP_BITS[dtype]).copy()
 
 
-def _quantize_fp8(x: torch.Tensor):
-    """Per-(b, h) amax/448 quantization to e4m3fn; returns (codes, descale[B*H])."""
-    B, H = x.shape[0], x.shape[1]
-    amax = x.abs().amax(dim=(2, 3)).to(torch.float32)
+def _quantize_fp8(x: torch.Tensor, tile: Optional[int] = None):
+    """amax/448 quantization to e4m3fn per (b, h), or per (b, h, tile of
+    `tile` rows); returns (codes, descales) with descales [B*H] or
+    [B*H*ceil(N/tile)] float32."""
+    B, H, N, d = x.shape
+    if tile:
+        nt = -(-N // tile)
+        xp = torch.zeros((B, H, nt * tile, d), dtype=torch.float32)
+        xp[:, :, :N] = x
+        amax = xp.reshape(B, H, nt, tile * d).abs().amax(dim=3)
+    else:
+        amax = x.abs().amax(dim=(2, 3))[:, :, None]
+    amax = amax.to(torch.float32)
     s = amax / torch.tensor(FP8_MAX, dtype=torch.float32)
     s = torch.where(amax > 0, s, torch.ones_like(s))
-    y = (x / s[:, :, None, None]).clamp(-FP8_MAX, FP8_MAX)
+    s_rows = s.repeat_interleave(tile, dim=2)[:, :, :N] if tile else s
+    y = (x / s_rows[:, :, :, None]).clamp(-FP8_MAX, FP8_MAX)
     codes = y.to(torch.float8_e4m3fn)
-    return _bits(codes, "fp8"), s.reshape(B * H).numpy().astype(np.float32)
+    return _bits(codes, "fp8"), s.reshape(-1).numpy().astype(np.float32)
 
 
 def from_float(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dtype: str,
                causal: bool = False, scale: Optional[float] = None,
-               seed: Optional[int] = None) -> AttnInputs:
-    """Round float32 tensors [B, H, N, d] to the storage type (RNE; fp8 quantized)."""
+               seed: Optional[int] = None, kv_tile: Optional[int] = None) -> AttnInputs:
+    """Round float32 tensors [B, H, N, d] to the storage type (RNE; fp8
+    quantized, K and V per tile of kv_tile rows when it is given)."""
     if dtype not in DTYPES:
         raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
     q, k, v = (t.detach().to("cpu", torch.float32).contiguous() for t in (q, k, v))
@@ -102,24 +119,27 @@ def from_float(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dtype: str,
     if scale is None:
         scale = default_scale(d)
     scale = float(np.float32(scale))
+    if kv_tile is not None and (dtype != "fp8" or int(kv_tile) < 1):
+        raise ValueError("kv_tile applies to fp8 inputs and must be >= 1")
     if dtype == "fp8":
-        (qb, dq), (kb, dk), (vb, dv) = (_quantize_fp8(t) for t in (q, k, v))
+        qb, dq = _quantize_fp8(q)
+        (kb, dk), (vb, dv) = (_quantize_fp8(t, kv_tile) for t in (k, v))
         return AttnInputs(B, H, N, d, dtype, bool(causal), scale, qb, kb, vb,
-                          dq, dk, dv, seed)
+                          dq, dk, dv, seed, kv_tile=int(kv_tile) if kv_tile else None)
     st = _TORCH_STORAGE[dtype]
     qb, kb, vb = (_bits(t.to(st), dtype) for t in (q, k, v))
     return AttnInputs(B, H, N, d, dtype, bool(causal), scale, qb, kb, vb, seed=seed)
 
 
 def draw(B: int, H: int, N: int, d: int, dtype: str, causal: bool, seed: int,
-         scale: Optional[float] = None) -> AttnInputs:
+         scale: Optional[float] = None, kv_tile: Optional[int] = None) -> AttnInputs:
     """The seeded iid N(0, 1) workload of the recipe above."""
     g = torch.Generator(device="cpu").manual_seed(int(seed))
     shape = (B, H, N, d)
     q = torch.randn(shape, generator=g, dtype=torch.float32)
     k = torch.randn(shape, generator=g, dtype=torch.float32)
     v = torch.randn(shape, generator=g, dtype=torch.float32)
-    return from_float(q, k, v, dtype, causal, scale, seed)
+    return from_float(q, k, v, dtype, causal, scale, seed, kv_tile)
 
 
 def draw_bwd(B: int, H: int, N: int, d: int, dtype: str, causal: bool, seed: int,

@@ -5,8 +5,14 @@ A step is one fa_fwd call over the whole workload (all of B x H x N query
 rows), inputs already resident in device memory.  Default workload: fp16,
 non-causal, B=2, H=16, N=4096, d=128 (the d=128 roofline workload).
 
+Timing: a fixed settle phase of back-to-back steps (--settle-s seconds, the
+time the package power limit needs to bring the clock to its steady state),
+then exactly --warmup untimed steps, then --reps windows of exactly --steps
+steps each, every window bracketed by a device synchronisation and timed with
+HIP events on the launch stream.  ms_per_step is the median window.
+
 Prints one JSON line:
-  value     counted TFLOPS = 4*B*H*N^2*d (halved if causal) / time per step
+  value     counted TFLOPS = 4*B*H*N^2*d (halved if causal) / median time per step
   roofline  the kernel against the MI355X dense MFMA peak of its input type,
             timed with HIP events on the stream the kernel is launched on
   clock     the graphics clock read from sysfs while the kernel runs back to
@@ -18,6 +24,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -32,10 +39,15 @@ DEFAULT_WORKLOAD = "fp16_b2h16_n4096_d128"
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000,
+                    help="steps per timed window (each window times exactly this many)")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps after the settle phase")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="timed windows; the median gives ms_per_step, the fastest ms_per_step_min")
     # The package power limit settles the clock only after a few tenths of a
-    # second of sustained load: warm up for ~0.6 s, then time ~0.3 s.
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=2000)
+    # second of sustained load.
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of back-to-back steps before the warm-up")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="workload name (attention_forward_fa_amd.inputs.CONFIGS, "
                          "EXTRA_WORKLOADS or SHARD_WORKLOADS)")
@@ -127,9 +139,43 @@ class ClockSampler:
         return sum(s) / len(s) if s else None
 
 
-def time_gpu(inp, steps, warmup, clock=None, layout="bhnd", pv8=None, kvsplit=False):
-    """Average seconds per fa_fwd call, HIP events on the launch stream; with a
-    ClockSampler, afterwards the mean graphics clock under the same load."""
+def timed_windows(step, steps, warmup, reps, settle_s):
+    """Runs step() back to back for settle_s seconds, then `warmup` untimed
+    times, then `reps` windows of exactly `steps` calls, each bracketed by a
+    device synchronisation and timed with HIP events recorded on the stream
+    the library launches on (torch's current stream).  Returns (seconds per
+    step of every window, settle seconds actually spent)."""
+    import torch
+
+    t0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(10):
+            step()
+        n_settle += 10
+        torch.cuda.synchronize()
+    settled = time.perf_counter() - t0
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    per_step = []
+    for _ in range(max(1, reps)):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        per_step.append(start.elapsed_time(end) * 1e-3 / steps)
+    return per_step, settled
+
+
+def fwd_step(inp, layout="bhnd", pv8=None, kvsplit=False):
+    """A closure running one forward pass over the workload, inputs and
+    outputs resident on the device (allocated here, before any timing)."""
     import torch
 
     from attention_forward_fa_amd import binding
@@ -166,26 +212,12 @@ def time_gpu(inp, steps, warmup, clock=None, layout="bhnd", pv8=None, kvsplit=Fa
         else:
             binding.fwd(q, k, v, causal=inp.causal, scale=inp.scale, out=out, lse=lse)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    sec = start.elapsed_time(end) * 1e-3 / steps
-    if clock is not None:
-        clock.mhz = clock.run(step, 1.0)
-    return sec
+    return step
 
 
-def time_gpu_bwd(inp, steps, warmup):
-    """Average seconds per fa_bwd call (the forward's O and LSE computed once
-    beforehand), HIP events on the launch stream."""
+def bwd_step(inp):
+    """A closure running one fa_bwd over the workload (the forward's O and LSE
+    computed once beforehand; gradients into preallocated buffers)."""
     import numpy as np
     import torch
 
@@ -198,27 +230,32 @@ def time_gpu_bwd(inp, steps, warmup):
     raw = np.ascontiguousarray(inp.do).view(np.int16)
     do = torch.from_numpy(raw).to("cuda").view(q.dtype)
     o, lse = binding.fwd(q, k, v, causal=inp.causal, scale=inp.scale)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for _ in range(3)]
+    delta = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
     def step():
-        binding.bwd(q, k, v, o, lse, do, causal=inp.causal, scale=inp.scale)
+        binding.bwd(q, k, v, o, lse, do, causal=inp.causal, scale=inp.scale,
+                    dq=grads[0], dk=grads[1], dv=grads[2], delta=delta)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3 / steps
+    return step
 
 
-def cpu_baseline(inp, budget_s):
-    """The oracle, as it stands, on whole heads of the workload until the budget runs out."""
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8", errors="replace"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(inp, budget_s, which="fwd"):
+    """The oracle, as it stands, on whole heads of the workload until the budget
+    runs out (forward: oracle.run; backward: oracle.run_bwd)."""
     import threadpoolctl
 
     from attention_forward_fa_amd import accounting
@@ -230,15 +267,21 @@ def cpu_baseline(inp, budget_s):
     t0 = time.perf_counter()
     heads = 0
     while heads < BH:
-        oracle.run(inp, heads=[heads])
+        if which == "bwd":
+            oracle.run_bwd(inp, heads=[heads])
+        else:
+            oracle.run(inp, heads=[heads])
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     flops = accounting.counted_flops(1, heads, inp.N, inp.d, inp.causal)
+    if which == "bwd":
+        flops *= 2.5
+    what = "gradients" if which == "bwd" else "query rows"
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOPS", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{heads} of {BH} heads, all {inp.N} query rows each, "
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"{heads} of {BH} heads, all {inp.N} {what} each, "
                       f"fp64 numpy/BLAS, {dt:.1f} s"}
 
 
@@ -299,30 +342,47 @@ def main(argv=None):
         inp = inputs.draw_bwd(B, H, N, d, dtype, causal, seed)
     else:
         inp = inputs.draw(B, H, N, d, dtype, causal, seed)
+    timing = dict(steps=args.steps, warmup=args.warmup, reps=args.reps, settle_s=args.settle_s)
     if args.which == "bwd":
         # Backward pass: 5 products of 2*N^2*d per head (2.5x the forward count).
-        steps, warmup = min(args.steps, 200), min(args.warmup, 100)
-        sec = time_gpu_bwd(inp, steps, warmup)
+        windows, settled = timed_windows(bwd_step(inp), **timing)
+        sec = statistics.median(windows)
         flops = 2.5 * acc.counted_flops(B, H, N, d, causal)
         tf = flops / sec / 1e12
         peak = acc.PEAK_TFLOPS[dtype]
-        print(json.dumps({
+        rec = {
             "metric": "attention bwd TFLOPS (10BHN²d/t, halved if causal), 1 GPU",
-            "value": round(tf, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": steps,
-            "warmup": warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
-            "dtype": {"fp16": "f16", "bf16": "bf16"}[dtype], "data": "synthetic",
+            "value": round(tf, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+            "ms_per_step_min": round(min(windows) * 1e3, 5), "reps": len(windows),
+            "windows_ms_per_step": [round(w * 1e3, 5) for w in windows],
+            "settle_s": round(settled, 3), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": {"fp16": "f16", "bf16": "bf16"}[dtype],
+            "data": "synthetic",
             "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "input_dtype": dtype,
-                       "causal": bool(causal), "gradients": "fp32"},
-            "frac_of_peak": round(tf / peak, 4)}), flush=True)
+                       "causal": bool(causal), "seed": seed, "gradients": "fp32"},
+            # One step is the dQ kernel then the fused dK/dV kernel; the
+            # roofline covers both (5 products counted over the step's time).
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
+                         "scope": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel"},
+        }
+        if not args.no_cpu_baseline:
+            rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, "bwd")
+        print(json.dumps(rec), flush=True)
         return 0
     clock = ClockSampler()
-    sec = time_gpu(inp, args.steps, args.warmup, clock, args.layout, args.fp8_pv, args.kvsplit)
+    step = fwd_step(inp, args.layout, args.fp8_pv, args.kvsplit)
+    windows, settled = timed_windows(step, **timing)
+    sec = statistics.median(windows)
+    clock.mhz = clock.run(step, 1.0)
     flops, tf, peak = describe(inp, sec)
     if args.sweep:
         for cfg in inputs.CONFIGS + inputs.EXTRA_WORKLOADS + inputs.SHARD_WORKLOADS:
             x = inputs.draw(*cfg[1:8])
-            s = time_gpu(x, max(10, args.steps // 4), args.warmup, None, args.layout,
-                         args.fp8_pv, args.kvsplit)
+            w, _ = timed_windows(fwd_step(x, args.layout, args.fp8_pv, args.kvsplit),
+                                 max(10, args.steps // 4), args.warmup, 3, 0.3)
+            s = statistics.median(w)
             _, t, pk = describe(x, s)
             print(json.dumps({"workload": cfg[0], "layout": args.layout,
                               "fp8_pv": args.fp8_pv if x.dtype == "fp8" else None,
@@ -338,6 +398,10 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(sec * 1e3, 5),
+        "ms_per_step_min": round(min(windows) * 1e3, 5),
+        "reps": len(windows),
+        "windows_ms_per_step": [round(w * 1e3, 5) for w in windows],
+        "settle_s": round(settled, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -23,8 +23,12 @@
  *
  * Conventions shared by every entry point:
  *   - q, k, v, o, lse and the descale arrays are DEVICE pointers owned by the
- *     caller; the library allocates, frees and retains nothing, keeps no
- *     global state and may be called from several host threads at once.
+ *     caller; the library allocates, frees and retains none of them and may
+ *     be called from several host threads at once.  Its only state is a
+ *     per-device cache of the current device's compute-unit and XCD counts
+ *     (read from the runtime on first use after a call's arguments have been
+ *     validated), which choose launch shapes and never change results
+ *     beyond rounding.
  *   - q, k, v: [B, H, N, d] contiguous, element type given by the dtype.
  *     o: [B, H, N, d] contiguous IEEE fp16 for every input dtype.
  *     lse: [B, H, N] contiguous fp32; required (never NULL when B*H*N > 0).

@@ -29,8 +29,8 @@ What it computes, and from which passages:
 
 Readings where the pages are silent:
   * all arithmetic in float64 from the exact input values (fp16 / bf16 widened
-    exactly; fp8 value = e4m3 code value x the float32 descale, both exact in
-    float64);
+    exactly; fp8 value = e4m3 code value x the float32 descale of its head, or
+    of its tile of key rows for K and V, both exact in float64);
   * masked scores are -inf; a row whose keys are all masked would have no
     softmax and is reported as O = 0, LSE = -inf (cannot happen with
     N_q == N_k, because the diagonal key is always kept);
@@ -87,27 +87,6 @@ E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
 def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     """OCP e4m3fn codes -> float64 values."""
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
-
-
-def dequantize(inp):
-    """Exact float64 Q, K, V of an input set (see the module docstring).
-
-    ``inp`` carries: dtype in {"fp16", "bf16", "fp8"}, storage bits q, k, v of
-    shape [B, H, N, d], and for fp8 the float32 descales [B*H].
-    """
-    if inp.dtype == "fp16":
-        return decode_fp16(inp.q), decode_fp16(inp.k), decode_fp16(inp.v)
-    if inp.dtype == "bf16":
-        return decode_bf16(inp.q), decode_bf16(inp.k), decode_bf16(inp.v)
-    if inp.dtype == "fp8":
-        B, H = inp.B, inp.H
-        out = []
-        for codes, ds in ((inp.q, inp.descale_q), (inp.k, inp.descale_k),
-                          (inp.v, inp.descale_v)):
-            scale = np.asarray(ds, dtype=np.float32).astype(np.float64).reshape(B, H, 1, 1)
-            out.append(decode_e4m3(codes) * scale)
-        return tuple(out)
-    raise ValueError(f"unknown dtype {inp.dtype!r}")
 
 
 # ---------------------------------------------------------------------------
@@ -211,7 +190,16 @@ def attention_bwd_head(q, k, v, do, scale, causal, chunk=256):
 
 
 def head_values(inp, b, h):
-    """Exact float64 (q, k, v), each [N, d], of head (b, h) of an input set."""
+    """Exact float64 (q, k, v), each [N, d], of head (b, h) of an input set.
+
+    fp8: the value of an element is its e4m3 code value times the float32
+    dequantization scale of its (b, h) head, descale_*[b*H + h].  When the
+    input set has key tiles (``inp.kv_tile`` = T rows), K and V carry one scale
+    per tile of T consecutive rows instead -- the per-block K scale of "第 17 章
+    TMA + Warp Specialization 把 FA2 写到 SOTA" §17.7 (item 1), applied to V's
+    rows in the same way: row n of head (b, h) takes descale_k[(b*H + h)*nt
+    + n // T] with nt = ceil(N / T).  Q keeps its per-head scale.
+    """
     if inp.dtype == "fp16":
         dec = decode_fp16
         return dec(inp.q[b, h]), dec(inp.k[b, h]), dec(inp.v[b, h])
@@ -220,9 +208,19 @@ def head_values(inp, b, h):
         return dec(inp.q[b, h]), dec(inp.k[b, h]), dec(inp.v[b, h])
     if inp.dtype == "fp8":
         f = b * inp.H + h
-        return tuple(decode_e4m3(c[b, h]) * float(np.float32(ds[f]))
-                     for c, ds in ((inp.q, inp.descale_q), (inp.k, inp.descale_k),
-                                   (inp.v, inp.descale_v)))
+        q = decode_e4m3(inp.q[b, h]) * float(np.float32(inp.descale_q[f]))
+        tile = getattr(inp, "kv_tile", None)
+        if not tile:
+            k = decode_e4m3(inp.k[b, h]) * float(np.float32(inp.descale_k[f]))
+            v = decode_e4m3(inp.v[b, h]) * float(np.float32(inp.descale_v[f]))
+            return q, k, v
+        nt = -(-inp.N // tile)
+        row_tile = f * nt + np.arange(inp.N) // tile
+        out = [q]
+        for codes, ds in ((inp.k, inp.descale_k), (inp.v, inp.descale_v)):
+            s = np.asarray(ds, dtype=np.float32).astype(np.float64)[row_tile]
+            out.append(decode_e4m3(codes[b, h]) * s[:, None])
+        return tuple(out)
     raise ValueError(f"unknown dtype {inp.dtype!r}")
 
 

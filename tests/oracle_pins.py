@@ -378,6 +378,65 @@ def pin_bwd_closed_forms():
     _close(dv[n - 1], p_last * do[n - 1], 1e-13, 0, "causal last key: dV")
 
 
+def _fp8_input(B, H, N, d, seed, kv_tile=None):
+    """An fp8 input set with random codes (NaN codes avoided) and distinct,
+    non-power-of-two float32 descales per head (or per key tile for K, V)."""
+    from attention_forward_fa_amd import inputs as I
+    rng = np.random.default_rng(seed)
+
+    def codes():
+        c = rng.integers(0, 256, size=(B, H, N, d), dtype=np.uint8)
+        return np.where((c & 0x7F) == 0x7F, c & 0xF0, c).astype(np.uint8)
+
+    nt = -(-N // kv_tile) if kv_tile else 1
+    ds_q = np.float32(1e-3) * (1 + np.arange(B * H, dtype=np.float32) * np.float32(0.37))
+    ds_k = np.float32(7e-4) * (1 + np.arange(B * H * nt, dtype=np.float32) * np.float32(0.29))
+    ds_v = np.float32(3e-3) * (1 + np.arange(B * H * nt, dtype=np.float32) * np.float32(0.53))
+    return I.AttnInputs(B, H, N, d, "fp8", False, float(np.float32(0.5)), codes(), codes(),
+                        codes(), ds_q.astype(np.float32), ds_k.astype(np.float32),
+                        ds_v.astype(np.float32), seed, kv_tile=kv_tile)
+
+
+def _fp8_values_independent(inp):
+    """Dequantized Q, K, V [B][H][N][d] as nested lists: codes decoded by torch's
+    float8_e4m3fn conversion, times the scale looked up element by element."""
+    dec = [torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn)
+           .to(torch.float64).numpy() for c in (inp.q, inp.k, inp.v)]
+    nt = -(-inp.N // inp.kv_tile) if inp.kv_tile else 1
+    out = []
+    for which, (x, ds) in enumerate(zip(dec, (inp.descale_q, inp.descale_k, inp.descale_v))):
+        t = [[[[0.0] * inp.d for _ in range(inp.N)] for _ in range(inp.H)] for _ in range(inp.B)]
+        for b in range(inp.B):
+            for h in range(inp.H):
+                for n in range(inp.N):
+                    if which > 0 and inp.kv_tile:
+                        sc = float(ds[(b * inp.H + h) * nt + n // inp.kv_tile])
+                    else:
+                        sc = float(ds[b * inp.H + h])
+                    for c in range(inp.d):
+                        t[b][h][n][c] = float(x[b, h, n, c]) * sc
+        out.append(t)
+    return out
+
+
+def pin_fp8_dequantization():
+    # The fp8 path (codes x float32 scales): B = 2, H = 3 with a scale of its
+    # own for every head -- and, with key tiles of 2 rows, for every K / V
+    # tile -- against the 40-digit brute force on values decoded and scaled
+    # independently of the oracle.  A head index taken as h*B + b, a tile index
+    # taken modulo the tile count, or a scale on the wrong tensor, moves O.
+    for kv_tile in (None, 2):
+        inp = _fp8_input(2, 3, 5, 4, 1700 + (kv_tile or 0), kv_tile)
+        O, L = A.run(inp)
+        qv, kv, vv = _fp8_values_independent(inp)
+        for b in range(inp.B):
+            for h in range(inp.H):
+                Od, Ld = decimal_attention(qv[b][h], kv[b][h], vv[b][h], inp.scale, False)
+                f = b * inp.H + h
+                _close(O[f], Od, 1e-12, 1e-12, f"fp8 O head {b},{h} kv_tile={kv_tile}")
+                _close(L[f], Ld, 1e-12, 1e-12, f"fp8 LSE head {b},{h} kv_tile={kv_tile}")
+
+
 PINS = [
     pin_decimal_bruteforce,
     pin_decimal_large_scores,
@@ -394,6 +453,7 @@ PINS = [
     pin_score_overflow_stress,
     pin_fwd_layout,
     pin_lse_merge,
+    pin_fp8_dequantization,
     pin_bwd_finite_differences,
     pin_bwd_invariants,
     pin_bwd_closed_forms,

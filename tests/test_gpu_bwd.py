@@ -85,11 +85,20 @@ def test_bwd_small(dtype, d, causal, N):
     inp = inputs.draw_bwd(2, 3, N, d, dtype, causal, seed=3000 + N + d)
     dq, dk, dv, delta, o = run_bwd(inp)
     check_grads(inp, (dq, dk, dv))
-    # delta = rowsum(dO * O) of the O the forward returned.
-    dov = torch.from_numpy(
-        oracle.decode_fp16(inp.do) if dtype == "fp16" else oracle.decode_bf16(inp.do))
-    want = (dov * o.cpu().double()).sum(-1)
-    assert torch.allclose(delta.cpu().double(), want, rtol=1e-5, atol=1e-5)
+    # delta = rowsum(dO * O) against the oracle's O.  The GPU forms it from
+    # the forward's O, which meets |O - O_oracle| <= 4e-3 per element and
+    # 5e-4 on average, so |delta - D_oracle| <= 4e-3 sum_c |dO_ic| per row
+    # (and the mean over rows within 5e-4 of the mean of sum_c |dO_ic|), plus
+    # fp32 rounding of a d-term sum.
+    dov = (oracle.decode_fp16(inp.do) if dtype == "fp16" else oracle.decode_bf16(inp.do))
+    dov = dov.reshape(inp.B * inp.H, inp.N, inp.d)
+    o_ref, _ = oracle.run(inp)
+    want = (dov * o_ref).sum(-1)
+    got = delta.cpu().double().numpy().reshape(inp.B * inp.H, inp.N)
+    err = np.abs(got - want)
+    absdo = np.abs(dov).sum(-1)
+    assert (err <= 4e-3 * absdo + 1e-5).all(), float((err - 4e-3 * absdo).max())
+    assert err.mean() <= 5e-4 * absdo.mean() + 1e-6, (float(err.mean()), float(absdo.mean()))
 
 
 @pytest.mark.parametrize("d", [64, 128])

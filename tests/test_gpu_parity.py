@@ -186,12 +186,13 @@ def test_causal_row0_is_v0_exactly(dtype, d):
 @pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
 def test_large_scores(dtype):
     # Scores of order 100 (beyond fp32 exp overflow at ~88): the running max
-    # must be subtracted before exp.  Scores are float32 dot products, so the
-    # LSE bar here is relative to |LSE|: 1e-3 + 1e-4 |LSE|.
+    # must be subtracted before exp.  fp16 / bf16 keep the absolute bars.
     inp = inputs.draw(1, 2, 130, 64, dtype, False, seed=24, scale=4.0)
     o, l = to_np(*gpu_run(inp), inp)
     assert float(np.abs(l).max()) > 88.0
-    tol = (TOL[dtype][0], TOL[dtype][1], 1e-3 + 1e-4 * float(np.abs(l).max()))
+    tol = None
+    if dtype == "fp8":
+        tol = (TOL[dtype][0], TOL[dtype][1], 1e-3 + 1e-4 * float(np.abs(l).max()))
     check(inp, o, l, tol=tol)
 
 

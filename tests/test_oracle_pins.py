@@ -106,7 +106,51 @@ def _bwd_dq_dk_swapped(q, k, v, do, scale, causal, chunk=256):
     return dk, dq, dv
 
 
+_orig_head_values = A.head_values
+
+
+def _head_values_index_transposed(inp, b, h):
+    # descales of head (b, h) looked up at h*B + b instead of b*H + h
+    if inp.dtype != "fp8":
+        return _orig_head_values(inp, b, h)
+    import copy
+    alt = copy.copy(inp)
+    perm = np.array([hh * inp.B + bb for bb in range(inp.B) for hh in range(inp.H)])
+    nt = -(-inp.N // inp.kv_tile) if inp.kv_tile else 1
+    alt.descale_q = np.asarray(inp.descale_q)[perm]
+    rows = (perm[:, None] * nt + np.arange(nt)[None, :]).reshape(-1)
+    alt.descale_k = np.asarray(inp.descale_k)[rows]
+    alt.descale_v = np.asarray(inp.descale_v)[rows]
+    return _orig_head_values(alt, b, h)
+
+
+def _head_values_tile_modulo(inp, b, h):
+    # key tile of row n taken as n % nt instead of n // kv_tile
+    if inp.dtype != "fp8" or not inp.kv_tile:
+        return _orig_head_values(inp, b, h)
+    q, _, _ = _orig_head_values(inp, b, h)
+    nt = -(-inp.N // inp.kv_tile)
+    f = b * inp.H + h
+    idx = f * nt + np.arange(inp.N) % nt
+    k = A.decode_e4m3(inp.k[b, h]) * np.asarray(inp.descale_k, np.float64)[idx][:, None]
+    v = A.decode_e4m3(inp.v[b, h]) * np.asarray(inp.descale_v, np.float64)[idx][:, None]
+    return q, k, v
+
+
+def _head_values_v_scale_on_k(inp, b, h):
+    # V's scale applied to K and K's to V
+    q, k, v = _orig_head_values(inp, b, h)
+    if inp.dtype != "fp8":
+        return q, k, v
+    alt = __import__("copy").copy(inp)
+    alt.descale_k, alt.descale_v = inp.descale_v, inp.descale_k
+    return _orig_head_values(alt, b, h)
+
+
 MUTANTS = [
+    ("head_values", _head_values_index_transposed),
+    ("head_values", _head_values_tile_modulo),
+    ("head_values", _head_values_v_scale_on_k),
     ("_scores", _scores_no_scale),
     ("_scores", _scores_sqrt_scale),
     ("_scores", _scores_mask_diag),
