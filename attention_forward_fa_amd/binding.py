@@ -42,6 +42,10 @@ SIGNATURES = {
     "fa_fwd_kvsplit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                       ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       _P, _I64, _P]),
+    "fa_fwd_kvsplit_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
+                                              _I64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, _P]),
+    "fa_fwd_kvsplit_noalloc_max_bytes": (ctypes.c_int64, []),
     "fa_fwd_fp8_pv_kvsplit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
                                              _I64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                              _I64, _P, _I64, _P]),
@@ -298,6 +302,35 @@ def fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str =
                                 ws_bytes, stream)
     _check(st)
     return out, lse
+
+
+def fwd_kvsplit_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "bhnd",
+                        causal: bool = False, scale: Optional[float] = None,
+                        descales: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fa_fwd_kvsplit_noalloc: fwd_kvsplit with the split workspace in the
+    library's static device scratch (the library allocates nothing; pass out
+    and lse to allocate nothing here either)."""
+    B, H, N, d = _layout_shape(q, layout)
+    _validate(q, k, v)
+    dq, dk, dv = _descale_ptrs(q, descales, B, H)
+    out, lse = _outputs(q, out, lse, layout)
+    scale = _default_scale(d) if scale is None else float(scale)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_fwd_kvsplit_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(dq), _ptr(dk), _ptr(dv),
+                                        _ptr(out), _ptr(lse), B, H, N, d, scale,
+                                        int(bool(causal)), _TORCH_DTYPE_CODE[q.dtype],
+                                        LAYOUTS[layout], stream)
+    _check(st)
+    return out, lse
+
+
+def kvsplit_noalloc_max_bytes() -> int:
+    """Bytes of the static split workspace behind fwd_kvsplit_noalloc."""
+    return int(load_library().fa_fwd_kvsplit_noalloc_max_bytes())
 
 
 def fwd_fp8_pv_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, min_keys: int = 512,

@@ -49,6 +49,8 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "fa_common.h"
@@ -1361,6 +1363,34 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   }
 }
 
+// Split workspace of fa_fwd_kvsplit_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol); it passes the device address scratch_ptr() looks up.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this GPU's copy of scratch, looked up with
+// hipGetSymbolAddress on the first call on each device (with that device
+// current) and kept per device; NULL if the runtime refuses.
+void* scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* ptr = ptrs[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  ptrs[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1464,6 +1494,36 @@ extern "C" int fa_fwd_kvsplit(const void* q, const void* k, const void* v, const
              layout, stream, -1, &pl, workspace);
 }
 
+extern "C" int fa_fwd_kvsplit_noalloc(const void* q, const void* k, const void* v,
+                                      const float* descale_q, const float* descale_k,
+                                      const float* descale_v, void* o, float* lse, int64_t B,
+                                      int64_t H, int64_t N, int64_t d, float scale, int causal,
+                                      int dtype, int layout, void* stream) {
+  bool empty;
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, layout, &empty);
+  if (st != FA_OK || empty) return st;
+  if (dtype == FA_DTYPE_FP8_E4M3) {
+    const int given = (descale_q != nullptr) + (descale_k != nullptr) + (descale_v != nullptr);
+    if (given != 0 && given != 3) return FA_ERR_NULL;
+    if (given == 3 &&
+        (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
+      return FA_ERR_ALIGN;
+  } else {
+    descale_q = descale_k = descale_v = nullptr;
+  }
+  const SplitPlan pl = plan_split(B * H, N, d, causal != 0, dtype, device_topology().cus);
+  void* ws = nullptr;
+  if (pl.g > 0) {
+    if (pl.ws_bytes > kScratchBytes) return FA_ERR_SCRATCH;
+    ws = scratch_ptr();
+    if (!ws) return FA_ERR_LAUNCH;
+  }
+  return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal, dtype,
+             layout, stream, -1, &pl, ws);
+}
+
+extern "C" int64_t fa_fwd_kvsplit_noalloc_max_bytes(void) { return kScratchBytes; }
+
 extern "C" int fa_fwd_fp8_pv_kvsplit(const void* q, const void* k, const void* v,
                                      const float* descale_q, const float* descale_k,
                                      const float* descale_v, void* o, float* lse, int64_t B,
@@ -1508,6 +1568,9 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_LAYOUT: return "layout must be FA_LAYOUT_BHND or FA_LAYOUT_BNHD";
     case FA_ERR_MIN_KEYS: return "min_keys must be >= 0";
     case FA_ERR_WORKSPACE: return "workspace smaller than fa_fwd_kvsplit_workspace requires";
+    case FA_ERR_SCRATCH:
+      return "fa_fwd_kvsplit_noalloc: the split needs more workspace than the library's static "
+             "scratch holds (fa_fwd_kvsplit_noalloc_max_bytes); use fa_fwd_kvsplit";
     default: return "unknown status";
   }
 }

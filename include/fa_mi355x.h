@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum {
   FA_DTYPE_FP16 = 0,      /* IEEE binary16 */
@@ -73,7 +73,8 @@ typedef enum {
   FA_ERR_CAUSAL = -8,     /* causal not 0 or 1 */
   FA_ERR_LAYOUT = -9,     /* unknown tensor layout */
   FA_ERR_MIN_KEYS = -10,  /* fa_fwd_fp8_pv: min_keys negative */
-  FA_ERR_WORKSPACE = -11  /* fa_fwd_kvsplit: workspace_bytes too small or negative */
+  FA_ERR_WORKSPACE = -11, /* fa_fwd_kvsplit: workspace_bytes too small or negative */
+  FA_ERR_SCRATCH = -12    /* fa_fwd_kvsplit_noalloc: split needs more than the static scratch */
 } fa_status;
 
 /* Memory layout of q, k, v and o (lse is always [B, H, N]). */
@@ -190,6 +191,35 @@ int fa_fwd_kvsplit(const void* q, const void* k, const void* v,
                    int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                    int causal, int dtype, int layout, void* workspace,
                    int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_kvsplit_noalloc -- fa_fwd_kvsplit for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and split, with the
+ * split workspace in a static device array of the library instead of a
+ * caller buffer.  Arguments as for fa_fwd_kvsplit without workspace and
+ * workspace_bytes; the caller still passes every input and output.  The
+ * array holds fa_fwd_kvsplit_noalloc_max_bytes() bytes (64 MiB) on every
+ * GPU the library runs on, from the first call on that GPU until the
+ * process ends; a problem whose split needs more (fa_fwd_kvsplit_workspace)
+ * returns FA_ERR_SCRATCH before any launch, and one that is not split needs
+ * none.  The call itself allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine.  Its first call on each device looks up that
+ * device's array address (hipGetSymbolAddress); if the runtime refuses, it
+ * returns FA_ERR_LAUNCH.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's partial results (each call writes every part
+ * it reads, so nothing needs clearing): calls that overlap in time on one
+ * GPU -- concurrent streams, or several host threads -- race and give
+ * undefined results; serialize them.  Errors as for fa_fwd_kvsplit.
+ */
+int fa_fwd_kvsplit_noalloc(const void* q, const void* k, const void* v,
+                           const float* descale_q, const float* descale_k,
+                           const float* descale_v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                           int causal, int dtype, int layout, void* stream);
+
+/* Bytes of the static split workspace of fa_fwd_kvsplit_noalloc. */
+int64_t fa_fwd_kvsplit_noalloc_max_bytes(void);
 
 /*
  * fa_fwd_fp8_pv_kvsplit -- fa_fwd_fp8_pv with the key-range split of

@@ -342,3 +342,38 @@ def test_fa_fwd_fp8_pv_kvsplit_rejects(kw, status):
 def test_fa_fwd_fp8_pv_kvsplit_empty_is_a_noop():
     assert _call_pvsplit(N=0, q=None, k=None, v=None, o=None, lse=None, ws=None,
                          ws_bytes=0) == 0
+
+
+def _call_noalloc(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, dq=None, dk=None, dv=None, o=O, lse=L, B=1, H=4, N=8192, d=128,
+                scale=0.1, causal=1, dtype=1, layout=0, stream=None)
+    args.update(kw)
+    return lib.fa_fwd_kvsplit_noalloc(args["q"], args["k"], args["v"], args["dq"], args["dk"],
+                                      args["dv"], args["o"], args["lse"], args["B"], args["H"],
+                                      args["N"], args["d"], args["scale"], args["causal"],
+                                      args["dtype"], args["layout"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=5), "FA_ERR_LAYOUT"),
+    (dict(d=80), "FA_ERR_HEAD_DIM"),
+    (dict(scale=0.0), "FA_ERR_SCALE"),
+    (dict(o=None), "FA_ERR_NULL"),
+    (dict(q=Q + 8), "FA_ERR_ALIGN"),
+    (dict(dtype=2, dq=A + 0x5000), "FA_ERR_NULL"),
+    # fp8 causal [1, 4, 16384, 128] splits into 81.25 MiB of partials: more
+    # than the 64 MiB static scratch, refused before any launch
+    (dict(dtype=2, N=16384), "FA_ERR_SCRATCH"),
+])
+def test_fa_fwd_kvsplit_noalloc_rejects(kw, status):
+    assert _call_noalloc(**kw) == _header_constants()[status]
+
+
+def test_fa_fwd_kvsplit_noalloc_empty_is_a_noop():
+    assert _call_noalloc(N=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert _call_noalloc(B=0) == 0
+
+
+def test_noalloc_scratch_size():
+    assert binding.kvsplit_noalloc_max_bytes() == 64 << 20
