@@ -34,10 +34,15 @@
 //   * software pipeline: iteration j issues the loads of K(j+3) and V(j+1)
 //     and, in one run of MFMAs, P V of block j-1 followed by QK^T of block
 //     j+1, with the softmax of block j and the V^T store of block j placed
-//     between the MFMAs; one workgroup barrier per block;
-//   * the reference max of a row only moves when a block max exceeds it by
-//     more than 2^8, so the O rescale is skipped for almost every block
-//     (probabilities then stay <= 2^8 and O, l remain consistent);
+//     between the MFMAs -- one matrix instruction per slice of the run, each
+//     followed by a few vector instructions whose inputs are a slice old;
+//     one workgroup barrier per block;
+//   * the probabilities of a row are taken against a reference that starts
+//     at the first block's max and moves only when a block's fp16
+//     probabilities would approach the top of the fp16 range (a row-sum
+//     check per block; the block is then redone against its own max), so no
+//     per-block max reduction runs in the loop and O, l stay consistent
+//     (fp8 P V keeps a per-block max: it sets the e4m3 scale);
 //   * workgroups are mapped to XCDs by head so the query tiles of a head,
 //     which all read the same K and V, share one L2.
 // Further modes of the same kernel: a 4-wave twin of the 8-wave kernels for
@@ -52,6 +57,7 @@
 
 #include <atomic>
 #include <stdint.h>
+#include <type_traits>
 
 #include "fa_common.h"
 #include "fa_mi355x.h"
@@ -132,22 +138,12 @@ __device__ __forceinline__ f32x16 mfma_pv8(const i32x8& a, const i32x8& b, int s
 
 
 
-// As above, with VPM VALU instructions placed after every MFMA: the MFMA
-// runs for 32+ cycles while the wave issues independent VALU work.
-template <int NM, int RPM, int LA, int VPM>
-__device__ __forceinline__ void mfma_read_valu_pipeline() {
-  static_assert(LA <= NM, "look-ahead longer than the run");
-  __builtin_amdgcn_sched_group_barrier(0x100, RPM * LA, 0);  // DS reads
-#pragma unroll
-  for (int i = 0; i < NM - LA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
-  }
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+// f(integral_constant<int, I>) for I = B .. E-1, in order (compile-time loop).
+template <int I, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
   }
 }
 
@@ -526,12 +522,15 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   f32x16 acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
-  // m_run: the reference max of this query's raw scores q.k that probabilities
-  // are taken against.  It only moves when the block max exceeds it by more
-  // than kRescaleLog2 in log2 units: until then p = exp2(c s - c m_run) stays
-  // <= 2^kRescaleLog2 and O, l are consistent without a rescale.
+  // Reference of this query's probabilities, p = exp2(c s - ref).  fp16 P V:
+  // ref_c = ref in log2 units, set from the first block's max and moved only
+  // when a block's fp16 probabilities would come near the top of the fp16
+  // range (the optimistic softmax below).  fp8 P V: m_run = ref / c in raw
+  // score units, moved when a block max exceeds it by more than kRescaleLog2
+  // in log2 units (so p <= 2^kRescaleLog2).
+  float ref_c = 0.0f;
   float m_run = -INFINITY;
-  float l_run = 0.0f;  // this lane's share of the row sum, relative to m_run
+  float l_run = 0.0f;  // this lane's share of the row sum, relative to the reference
   // P as fp16 pairs, the B operand of O^T += V^T P^T: [key tile][k-step][dword].
   typedef uint32_t PRegs[2][2][4];
   // fp8 P V: P as 32 e4m3 codes (byte 16*kt + i = accumulator element i of key
@@ -576,27 +575,25 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
       }
   };
 
-  // Online softmax of one block: new reference max (branch-free select),
-  // P as fp16 pairs laid out as the B operand of O^T += V^T P^T, row-sum
-  // update.  Returns the factor O^T must be scaled by when `rescale`.
-  auto softmax = [&](f32x16* st, PRegs& pw, bool& rescale) __attribute__((always_inline)) -> float {
-    float m0 = st[0][0], m1 = st[1][0];  // two independent chains
-#pragma unroll
-    for (int i = 1; i < 15; i += 2) {
-      m0 = vmax(vmax(m0, st[0][i]), st[0][i + 1]);
-      m1 = vmax(vmax(m1, st[1][i]), st[1][i + 1]);
-    }
-    const float mx = max_pair32(vmax(vmax(m0, st[0][15]), vmax(m1, st[1][15])));
-    rescale = __builtin_amdgcn_ballot_w64((mx - m_run) * c > kRescaleLog2) != 0;
-    const float m_use = rescale ? vmax(m_run, mx) : m_run;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-    m_run = m_use;
-    // p = exp2(c s - c m): all FMAs, then all exponentials, in place.
-    const float nmc = -m_use * c;
+  // Online softmax of one block against the current reference (fp16 P V), the
+  // optimistic form: no block max is taken.  p = exp2(c s - ref_c) rounded to
+  // fp16 pairs laid out as the B operand of O^T += V^T P^T, and the lane's
+  // share of the block's row sum over those fp16 values.  Any reference keeps
+  // O and l consistent (both scale alike), so ref_c only has to keep every p
+  // finite and well inside the fp16 range: while the lane's share stays below
+  // 2^15, every p does.  Returns that share; a lane at or above it (or NaN /
+  // inf) sends the wave through rescale_block below.  The row's true max
+  // enters only through the first block (ref_c starts at its max) and those
+  // rare rescales, so the per-block chain max -> lane exchange -> exp of the
+  // usual online softmax, and its VALU work, drop out of the loop.
+  constexpr float kRowSumCap = 32768.0f;
+  auto softmax = [&](f32x16* st, PRegs& pw) __attribute__((always_inline)) -> float {
+    const float nref = -ref_c;
+    // p = exp2(c s - ref): all FMAs, then all exponentials, in place.
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[kt][i] = fmaf(st[kt][i], c, nmc);
+      for (int i = 0; i < 16; ++i) st[kt][i] = fmaf(st[kt][i], c, nref);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -618,8 +615,18 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
         for (int w = 0; w < 4; ++w)
           part[w] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[kt][s][w]), ones, part[w],
                                            false);
-    l_run = l_run * alpha + ((part[0] + part[1]) + (part[2] + part[3]));
-    return alpha;
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+
+  // Raw scores' max over the block for this query (both lanes of the pair).
+  auto block_max = [&](const f32x16* st) __attribute__((always_inline)) -> float {
+    float m0 = st[0][0], m1 = st[1][0];  // two independent chains
+#pragma unroll
+    for (int i = 1; i < 15; i += 2) {
+      m0 = vmax(vmax(m0, st[0][i]), st[0][i + 1]);
+      m1 = vmax(vmax(m1, st[1][i]), st[1][i + 1]);
+    }
+    return max_pair32(vmax(vmax(m0, st[0][15]), vmax(m1, st[1][15])));
   };
 
   // O^T += V^T P^T for the block in V buffer vbuf.  Slot i of lane half hh
@@ -744,48 +751,146 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     f32x16 sa[2], sb[2];
     PRegs pa, pb = {};
     qk(k_lds0, sa);
+    // The reference starts at the first block's max (every row has a key in
+    // the first block of its range, so it is finite).
+    if (needs_mask(kb_lo)) mask(sa, kb_lo * kBC);
+    ref_c = block_max(sa) * c;
     barrier();
 
     constexpr int NPV = NDT * 4;     // P V MFMAs per block
     constexpr int NQK = 2 * NKS;     // QK^T MFMAs per block
-    constexpr int VPM = (160 + NPV + NQK - 1) / (NPV + NQK);  // about 160 VALU per block
-    constexpr int TPM = (kBC / 2 + NPV + NQK) / (NPV + NQK);  // kBC / 2 + 1 exponentials per block
-    auto step = [&](int j, const uint8_t* k_next, uint8_t* k_fill, const uint8_t* v_prev,
-                    uint8_t* v_fill, f32x16* s_cur, f32x16* s_next, PRegs& p_cur,
-                    const PRegs& p_prev) __attribute__((always_inline)) {
+    // A block whose probabilities came too close to the top of the fp16 range
+    // against the current reference (rare: the first block sets it, and the
+    // fp16 range leaves 15 powers of two above it): S(j) again from K(j),
+    // which stays in its LDS stage until the next iteration's loads; the
+    // reference moves up to the block's max, O^T (which holds blocks up to
+    // j - 1 once this iteration's P V has run) and l scale by
+    // exp2(old - new), and P(j) is taken again.
+    auto rescale_block = [&](int j, const uint8_t* k_cur, f32x16* st, PRegs& p_cur) __attribute__((always_inline)) -> float {
+      qk(k_cur, st);  // into the registers of the block's spent fp32 probabilities
+      mfma_read_pipeline<NQK, KCH, 1>();  // one operand read ahead: few registers in flight
+      if (needs_mask(j)) mask(st, j * kBC);
+      const float ref_new = vmax(ref_c, block_max(st) * c);  // a fully masked row keeps ref_c
+      const float alpha = __builtin_amdgcn_exp2f(ref_c - ref_new);
+      ref_c = ref_new;
+      const float ls = softmax(st, p_cur);
+      l_run = l_run * alpha + ls;
+      return alpha;
+    };
+    // One iteration as an explicit software pipeline of NM slices.  Slice m
+    // issues matrix instruction m of the run (P V of block j-1, then QK^T of
+    // block j+1), the LDS operand reads of instruction m + LA, and slice m's
+    // share of block j's softmax: score i's FMA in slice ~i*NM/32 - 1, its
+    // exponential one slice later, the fp16 pack of a pair and its row-sum dot
+    // product one and two slices after that.  A scheduling barrier closes
+    // every slice, so each wave's stream alternates one matrix instruction
+    // with a few independent vector instructions whose inputs were produced
+    // at least a slice earlier -- the mix two waves of a SIMD overlap best
+    // (matrix pipe busy while the other wave's vector work issues) -- instead
+    // of runs of dependent vector work between runs of matrix instructions.
+    constexpr int NM = NPV + NQK;
+    constexpr int LA = 4;                          // operand reads issued ahead
+    constexpr int OW = KCH * 4;                    // dwords of one operand
+    static_assert(NM >= 8, "run too short for the slice schedule");
+    auto fma_slice = [](int i) { return (i * NM) / 32 - 1; };  // slices -1 .. NM-1
+    auto step = [&](int j, const uint8_t* k_cur, const uint8_t* k_next, uint8_t* k_fill,
+                    const uint8_t* v_prev, uint8_t* v_fill, f32x16* s_cur, f32x16* s_next,
+                    PRegs& p_cur, const PRegs& p_prev) __attribute__((always_inline)) {
       if (needs_mask(j)) mask(s_cur, j * kBC);
-      store_v(vst, v_fill);             // V(j) -> V^T
-      load_v((j + 1) * kBC, vst);       // V(j+1) -> registers
-      // V(j+1) goes out before K(j+3): the wait for V(j+1) where it is stored
-      // then leaves K(j+3) in flight.
+      uint32_t opnd[LA][OW];                       // operand ring, slot m % LA
+      auto read = [&](auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m < NPV) {
+          constexpr int kt = m / (2 * NDT), sidx = (m / NDT) % 2, t = m % NDT;
+          const u32x4 x = *reinterpret_cast<const u32x4*>(
+              v_prev + vt_raddr + t * 32 * VTROW + (kt * 32 + 16 * sidx) * 2);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) opnd[m % LA][w] = x[w];
+        } else {
+          constexpr int q = m - NPV, ks = q / 2, kt = q % 2;
+#pragma unroll
+          for (int u = 0; u < KCH; ++u) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(k_next + kt * 32 * KROWB + k_raddr[ks][u]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) opnd[m % LA][4 * u + w] = x[w];
+          }
+        }
+      };
+      auto mfma = [&](auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m < NPV) {
+          constexpr int kt = m / (2 * NDT), sidx = (m / NDT) % 2, t = m % NDT;
+          const u32x4 a = {opnd[m % LA][0], opnd[m % LA][1], opnd[m % LA][2], opnd[m % LA][3]};
+          const u32x4 b = {p_prev[kt][sidx][0], p_prev[kt][sidx][1], p_prev[kt][sidx][2],
+                           p_prev[kt][sidx][3]};
+          acc[t] = mfma_pv(a, b, acc[t]);
+        } else {
+          constexpr int q = m - NPV, ks = q / 2, kt = q % 2;
+          QKOperand<DT> a;
+#pragma unroll
+          for (int w = 0; w < OW; ++w) a.w[w] = opnd[m % LA][w];
+          s_next[kt] = mfma_qk<DT>(a, qreg[ks], ks == 0 ? f32x16{} : s_next[kt]);
+        }
+      };
+      const float nref = -ref_c;
+      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+      auto softmax_slice = [&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (fma_slice(i) == k) s_cur[i / 16][i % 16] = fmaf(s_cur[i / 16][i % 16], c, nref);
+          if (fma_slice(i) + 1 == k) s_cur[i / 16][i % 16] = __builtin_amdgcn_exp2f(s_cur[i / 16][i % 16]);
+          if (i % 2 == 1 && fma_slice(i) + 2 == k) {
+            const int kt = i / 16, e = i % 16 - 1;
+            p_cur[kt][e / 8][(e % 8) / 2] = pack_f16x2(s_cur[kt][e], s_cur[kt][e + 1]);
+          }
+          if (i % 2 == 1 && fma_slice(i) + 3 == k) {
+            const int kt = i / 16, e = i % 16 - 1, pi = i / 2;
+            part[pi % 4] = __builtin_amdgcn_fdot2(
+                __builtin_bit_cast(f16x2, p_cur[kt][e / 8][(e % 8) / 2]), ones, part[pi % 4], false);
+          }
+        }
+      };
+      // slice -1: the first LA operand reads and the first scores' FMAs
+      static_for<0, LA>(read);
+      softmax_slice(std::integral_constant<int, -1>{});
       __builtin_amdgcn_sched_barrier(0);
-      load_k((j + 3) * kBC, k_fill);    // K(j+3)
-      pv(v_prev, p_prev);               // P V of block j-1
-      qk(k_next, s_next);               // QK^T of block j+1
-      bool rescale;
-      const float alpha = softmax(s_cur, p_cur, rescale);
-      mfma_run_pipeline<NPV, 1, NQK, KCH, 4, VPM, TPM, 0, K_PER_W>();
-      // Keep the softmax in this block, beside the MFMAs: its results are only
-      // used next iteration, and the compiler would otherwise sink it there.
-  #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-  #pragma unroll
-        for (int s = 0; s < 2; ++s)
-  #pragma unroll
-          for (int w = 0; w < 4; ++w) asm volatile("" ::"v"(p_cur[kt][s][w]));
-      asm volatile("" ::"v"(l_run));
-      if (rescale) {  // after P V(j-1): all of O^T is relative to the old max
-  #pragma unroll
+      static_for<0, NM + 3>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < NM) mfma(kc);
+        if constexpr (k + LA < NM) read(std::integral_constant<int, k + LA>{});
+        softmax_slice(kc);
+        if constexpr (k == 0) store_v(vst, v_fill);            // V(j) -> V^T
+        if constexpr (k == 2) load_v((j + 1) * kBC, vst);      // V(j+1) -> registers
+        if constexpr (k == 4) load_k((j + 3) * kBC, k_fill);   // K(j+3), after V(j+1)
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      const float ls = (part[0] + part[1]) + (part[2] + part[3]);
+      const bool big = __builtin_amdgcn_ballot_w64(!(ls < kRowSumCap)) != 0;
+      float alpha = 1.0f;
+      if (big) {
+        alpha = rescale_block(j, k_cur, s_cur, p_cur);
+      } else {
+        l_run += ls;
+      }
+      // O^T holds blocks up to j - 1 now (this iteration's P V has run), all
+      // relative to the old reference.  (A branch of its own: inside the one
+      // above, the accumulators' rescale next to the matrix instructions there
+      // cost the loop ~40 registers.)
+      asm volatile("" ::: "memory");
+      if (big) {
+#pragma unroll
         for (int t = 0; t < NDT; ++t) acc[t] *= alpha;
       }
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVM) : "memory");
       barrier();
     };
     // Iteration j with j % 4 == 0, 1, 2, 3.
-    auto step0 = [&](int j) __attribute__((always_inline)) { step(j, k_lds1, k_lds3, v_lds1, v_lds0, sa, sb, pa, pb); };
-    auto step1 = [&](int j) __attribute__((always_inline)) { step(j, k_lds2, k_lds0, v_lds0, v_lds1, sb, sa, pb, pa); };
-    auto step2 = [&](int j) __attribute__((always_inline)) { step(j, k_lds3, k_lds1, v_lds1, v_lds0, sa, sb, pa, pb); };
-    auto step3 = [&](int j) __attribute__((always_inline)) { step(j, k_lds0, k_lds2, v_lds0, v_lds1, sb, sa, pb, pa); };
+    auto step0 = [&](int j) __attribute__((always_inline)) { step(j, k_lds0, k_lds1, k_lds3, v_lds1, v_lds0, sa, sb, pa, pb); };
+    auto step1 = [&](int j) __attribute__((always_inline)) { step(j, k_lds1, k_lds2, k_lds0, v_lds0, v_lds1, sb, sa, pb, pa); };
+    auto step2 = [&](int j) __attribute__((always_inline)) { step(j, k_lds2, k_lds3, k_lds1, v_lds1, v_lds0, sa, sb, pa, pb); };
+    auto step3 = [&](int j) __attribute__((always_inline)) { step(j, k_lds3, k_lds0, k_lds2, v_lds0, v_lds1, sb, sa, pb, pa); };
     auto last_pv = [&](const uint8_t* vbuf, const PRegs& p_last) __attribute__((always_inline)) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS load outlives the loop
       pv(vbuf, p_last);
@@ -940,7 +1045,8 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
       const u32x4 x = *reinterpret_cast<const u32x4*>(obuf + r * OROWB + ((ch ^ (r % OCH)) * 16));
       if (qw0 + r < N) *reinterpret_cast<u32x4*>(wrows + r * wstride + ch * 8) = x;
     }
-    if (hh == 0 && my_q < N) wlse[lr] = kLn2 * (m_run * c + __builtin_amdgcn_logf(l_tot));
+    const float ref_log2 = PV8 ? m_run * c : ref_c;
+    if (hh == 0 && my_q < N) wlse[lr] = kLn2 * (ref_log2 + __builtin_amdgcn_logf(l_tot));
   }
 }
 
