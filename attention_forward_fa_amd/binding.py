@@ -37,6 +37,8 @@ SIGNATURES = {
                                  ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]),
     "fa_fwd_fp8_pv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                      ctypes.c_float, ctypes.c_int, ctypes.c_int, _I64, _P]),
+    "fa_fwd_fp8_kvtile": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, _I64, _P]),
     "fa_fwd_kvsplit_workspace": (ctypes.c_int64, [_I64, _I64, _I64, _I64, ctypes.c_int,
                                                    ctypes.c_int]),
     "fa_fwd_kvsplit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
@@ -255,6 +257,42 @@ def fwd_fp8_pv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, min_keys: int 
     return out, lse
 
 
+KV_TILE = 64  # key rows per scale of fa_fwd_fp8_kvtile
+
+
+def fwd_fp8_kvtile(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   descales: Tuple[torch.Tensor, torch.Tensor, torch.Tensor],
+                   pv_min_keys: int = -1, layout: str = "bhnd", causal: bool = False,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fa_fwd_fp8_kvtile: float8_e4m3fn q, k, v; descales = (per-head Q scales
+    [B*H], per-tile K scales [B*H*ceil(N/64)], per-tile V scales, float32
+    device tensors).  pv_min_keys < 0 keeps P V in fp16."""
+    B, H, N, d = _layout_shape(q, layout)
+    _validate(q, k, v)
+    if q.dtype != torch.float8_e4m3fn:
+        raise TypeError("fwd_fp8_kvtile takes float8_e4m3fn q, k, v")
+    nt = -(-N // KV_TILE)
+    want = (B * H, B * H * nt, B * H * nt)
+    if descales is None or len(descales) != 3:
+        raise ValueError("fwd_fp8_kvtile needs (descale_q, descale_k, descale_v)")
+    for t, n in zip(descales, want):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() != n
+                or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"descales must be contiguous float32 device tensors of "
+                             f"{want} elements")
+    out, lse = _outputs(q, out, lse, layout)
+    scale = _default_scale(d) if scale is None else float(scale)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.fa_fwd_fp8_kvtile(_ptr(q), _ptr(k), _ptr(v), *(_ptr(t) for t in descales),
+                                   _ptr(out), _ptr(lse), B, H, N, d, scale, int(bool(causal)),
+                                   LAYOUTS[layout], int(pv_min_keys), stream)
+    _check(st)
+    return out, lse
+
+
 def kvsplit_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool, dtype) -> int:
     """fa_fwd_kvsplit_workspace: device bytes fwd_kvsplit needs (0: it will not split)."""
     code = _TORCH_DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
@@ -427,8 +465,13 @@ def to_device(inp, device="cuda"):
 
 
 def run_inputs(inp, device="cuda", out=None, lse=None):
-    """Run the library on an input set (fp8 with its per-head descales)."""
+    """Run the library on an input set (fp8 with its per-head descales, or
+    fa_fwd_fp8_kvtile when K and V carry per-key-tile scales)."""
     q, k, v, ds = to_device(inp, device)
+    if inp.dtype == "fp8" and getattr(inp, "kv_tile", None):
+        if inp.kv_tile != KV_TILE:
+            raise ValueError(f"the library takes key tiles of {KV_TILE} rows")
+        return fwd_fp8_kvtile(q, k, v, ds, causal=inp.causal, scale=inp.scale, out=out, lse=lse)
     if inp.dtype == "fp8":
         return fwd_fp8(q, k, v, *ds, causal=inp.causal, scale=inp.scale, out=out, lse=lse)
     return fwd(q, k, v, causal=inp.causal, scale=inp.scale, out=out, lse=lse)

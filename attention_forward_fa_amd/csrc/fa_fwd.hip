@@ -176,8 +176,10 @@ __device__ __forceinline__ void mfma_run_pipeline() {
 
 // Two consecutive storage elements of V (one dword, fp16 or bf16) as fp16x2;
 // or, for fp8, two e4m3 codes from the low / high 16 bits of a dword.
+// fp8 codes are multiplied by the power of two pow2 (exact unless the result
+// leaves the fp16 range).
 template <int DT, bool HI_WORD>
-__device__ __forceinline__ uint32_t v_pair_to_f16(uint32_t w) {
+__device__ __forceinline__ uint32_t v_pair_to_f16(uint32_t w, float pow2 = 1.0f) {
   if constexpr (DT == FA_DTYPE_FP16) {
     return w;
   } else if constexpr (DT == FA_DTYPE_BF16) {
@@ -187,7 +189,8 @@ __device__ __forceinline__ uint32_t v_pair_to_f16(uint32_t w) {
     float hi = __uint_as_float(w & 0xffff0000u);
     return pack_f16x2(lo, hi);
   } else {
-    f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI_WORD);  // exact
+    // The conversion's scale operand contributes its exponent only.
+    f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, pow2, HI_WORD);  // exact
     return __builtin_bit_cast(uint32_t, h);
   }
 }
@@ -220,6 +223,9 @@ struct Params {
   int split_cmax;
   _Float16* ws_o;
   float* ws_lse;
+  // Per-key-tile fp8 scales (kernels with KVT): descale_k and descale_v hold
+  // one scale per tile of kBC key rows, head bh's tile t at bh * n_kvt + t.
+  int n_kvt;
 };
 
 
@@ -241,8 +247,9 @@ __device__ __forceinline__ int vswz8(int row) {
 
 // PV8: fp8 inputs with P V on the fp8 matrix cores too (V kept as e4m3 in
 // LDS, P rounded to e4m3 under a per-row power-of-two scale); otherwise P V
-// runs in fp16.
-template <int DT, int D, bool CAUSAL, int WAVES, bool PV8 = false>
+// runs in fp16.  KVT: fp8 with K and V dequantization scales per key tile
+// (one per block of kBC keys) instead of per head.
+template <int DT, int D, bool CAUSAL, int WAVES, bool PV8 = false, bool KVT = false>
 __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int kWaves = Shape<WAVES>::waves;
@@ -266,6 +273,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   constexpr int VIN = VD * ES;            // input bytes per key row per staging thread
   static_assert(kBC * D == 4 * VD * kThreads, "V staging must tile the workgroup");
   static_assert(!PV8 || (DT == FA_DTYPE_FP8_E4M3 && WAVES == 4), "fp8 P V: fp8, four waves");
+  static_assert(!KVT || DT == FA_DTYPE_FP8_E4M3, "per-tile scales: fp8 only");
   // fp16 P V: two V^T stages; fp8 P V: four stages of V rows as loaded.
   constexpr int VSTAGE = PV8 ? KBUF : VBUF;
 
@@ -344,10 +352,40 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   float v_scale = 1.0f;
   if constexpr (DT == FA_DTYPE_FP8_E4M3) {
     if (p.descale_q) {
-      c *= p.descale_q[bh] * p.descale_k[bh];
-      v_scale = p.descale_v[bh];
+      c *= p.descale_q[bh];
+      if constexpr (!KVT) {
+        c *= p.descale_k[bh];
+        v_scale = p.descale_v[bh];
+      }
     }
   }
+  // Per-key-tile scales of block j (KVT).  K's scale multiplies the block's
+  // scores: cb = c * descale_k.  V's scale dv = 2^ev * f, f in [1, 2), is
+  // split: 2^ev is applied exactly where V's e4m3 values are converted to
+  // fp16 (or, for fp8 P V, in the matrix instruction's E8M0 scale of P) and f
+  // multiplies the block's probabilities inside their exponential (log2 f
+  // added to the exponent), the row sum dividing it out again.  Scales must
+  // be positive normal floats.
+  struct TileScale {
+    float cb = 0.0f, lf = 0.0f, inv_f = 1.0f, vp2 = 1.0f;
+    int ev = 0;
+  };
+  auto tile_scale = [&](int j) __attribute__((always_inline)) {
+    TileScale t;
+    if constexpr (KVT) {
+      const int64_t i = (int64_t)bh * p.n_kvt + min(j, p.n_kvt - 1);  // blocks past N: any tile's
+      const uint32_t vb = __float_as_uint(p.descale_v[i]);
+      t.cb = c * p.descale_k[i];
+      t.vp2 = __uint_as_float(vb & 0xff800000u);                 // 2^ev
+      const float f = __uint_as_float((vb & 0x007fffffu) | 0x3f800000u);  // [1, 2)
+      t.lf = __builtin_amdgcn_logf(f);
+      t.inv_f = __builtin_amdgcn_rcpf(f);
+      t.ev = (int)((vb >> 23) & 0xffu) - 127;
+    } else {
+      t.cb = c;
+    }
+    return t;
+  };
 
   // ---- Q tile -> registers, the B operand of S^T = K Q^T (rows >= N read 0) --
   QKOperand<DT> qreg[NKS];
@@ -457,7 +495,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   };
   // Convert the 4 x VD block held in registers to fp16 and write its VD rows
   // of V^T into the V^T buffer vbuf.
-  auto store_v = [&](const VRegs& vst, uint8_t* vbuf) __attribute__((always_inline)) {
+  auto store_v = [&](const VRegs& vst, uint8_t* vbuf, float vp2) __attribute__((always_inline)) {
     uint32_t h[4][VD / 2];  // fp16 pairs along d, per key
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -466,9 +504,9 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
         if constexpr (ES == 2) {
           h[r][w] = v_pair_to_f16<DT, false>(vst[r][w]);
         } else if (w & 1) {
-          h[r][w] = v_pair_to_f16<DT, true>(vst[r][w / 2]);
+          h[r][w] = v_pair_to_f16<DT, true>(vst[r][w / 2], vp2);
         } else {
-          h[r][w] = v_pair_to_f16<DT, false>(vst[r][w / 2]);
+          h[r][w] = v_pair_to_f16<DT, false>(vst[r][w / 2], vp2);
         }
       }
     // v_perm_b32 picks bytes of {a, b} (b = bytes 0-3, a = bytes 4-7): the
@@ -522,14 +560,13 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   f32x16 acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
-  // Reference of this query's probabilities, p = exp2(c s - ref).  fp16 P V:
-  // ref_c = ref in log2 units, set from the first block's max and moved only
+  // Reference of this query's probabilities, p = exp2(c s - ref), in log2
+  // units.  fp16 P V: ref_c, set from the first block's max and moved only
   // when a block's fp16 probabilities would come near the top of the fp16
-  // range (the optimistic softmax below).  fp8 P V: m_run = ref / c in raw
-  // score units, moved when a block max exceeds it by more than kRescaleLog2
-  // in log2 units (so p <= 2^kRescaleLog2).
+  // range (the optimistic softmax below).  fp8 P V: ref8, moved when a block
+  // max exceeds it by more than kRescaleLog2 (so p <= 2^kRescaleLog2).
   float ref_c = 0.0f;
-  float m_run = -INFINITY;
+  float ref8 = -INFINITY;
   float l_run = 0.0f;  // this lane's share of the row sum, relative to the reference
   // P as fp16 pairs, the B operand of O^T += V^T P^T: [key tile][k-step][dword].
   typedef uint32_t PRegs[2][2][4];
@@ -558,7 +595,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   };
 
   // Keys past N, and (causal) keys after the query, get score -inf.  A block
-  // with every key masked for this lane leaves m_run, l_run unchanged and
+  // with every key masked for this lane leaves the reference and l_run unchanged and
   // contributes P = 0 (block 0 always holds a valid key for every row).
   auto needs_mask = [&](int j) __attribute__((always_inline)) {
     return (j * kBC + kBC > kv_end) || (CAUSAL && j * kBC + kBC - 1 > qw0);
@@ -587,13 +624,13 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
   // rare rescales, so the per-block chain max -> lane exchange -> exp of the
   // usual online softmax, and its VALU work, drop out of the loop.
   constexpr float kRowSumCap = 32768.0f;
-  auto softmax = [&](f32x16* st, PRegs& pw) __attribute__((always_inline)) -> float {
-    const float nref = -ref_c;
-    // p = exp2(c s - ref): all FMAs, then all exponentials, in place.
+  auto softmax = [&](f32x16* st, PRegs& pw, const TileScale& ts) __attribute__((always_inline)) -> float {
+    const float nref = ts.lf - ref_c;
+    // p = exp2(c s - ref) (times f, KVT): all FMAs, then all exponentials, in place.
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[kt][i] = fmaf(st[kt][i], c, nref);
+      for (int i = 0; i < 16; ++i) st[kt][i] = fmaf(st[kt][i], ts.cb, nref);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -648,32 +685,36 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
         }
   };
 
-  // fp8 P V softmax: as above, except that the probabilities of a row are
-  // taken as 2^k exp2(c s - c m) with k = 8 - ceil(c (block max - m)), which
-  // lifts the block's largest one into (2^7, 2^8] (e4m3 holds 3 fraction bits
-  // from 2^-6 to 448), rounded to e4m3, and the MFMA scales them back by 2^-k.
-  // The row sum takes the unrounded values.
-  auto softmax8 = [&](f32x16* st, P8Regs& pw, bool& rescale) __attribute__((always_inline)) -> float {
+  // fp8 P V softmax, in log2 units like the reference ref8: the row's block
+  // max (scaled) moves the reference when it passes it by more than
+  // kRescaleLog2; the probabilities are taken as 2^k exp2(cb s - ref8) (times
+  // f, KVT) with k = 8 - ceil(block max - ref8 (+ log2 f)), which lifts the
+  // block's largest one into (2^7, 2^8] (e4m3 holds 3 fraction bits from 2^-6
+  // to 448), rounded to e4m3, and the MFMA scales them back by 2^-k (and 2^ev,
+  // KVT).  The row sum takes the unrounded values.
+  auto softmax8 = [&](f32x16* st, P8Regs& pw, bool& rescale, const TileScale& ts)
+                      __attribute__((always_inline)) -> float {
     float m0 = st[0][0], m1 = st[1][0];
 #pragma unroll
     for (int i = 1; i < 15; i += 2) {
       m0 = vmax(vmax(m0, st[0][i]), st[0][i + 1]);
       m1 = vmax(vmax(m1, st[1][i]), st[1][i + 1]);
     }
-    const float mx = max_pair32(vmax(vmax(m0, st[0][15]), vmax(m1, st[1][15])));
-    rescale = __builtin_amdgcn_ballot_w64((mx - m_run) * c > kRescaleLog2) != 0;
-    const float m_use = rescale ? vmax(m_run, mx) : m_run;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-    m_run = m_use;
-    // (mx - m_use) c <= kRescaleLog2 = 8, so k >= 0; a row with no key in the
-    // block (mx = -inf) takes k = 64.
-    const float kf = fminf(8.0f - ceilf((mx - m_use) * c), 64.0f);
+    const float mxs = max_pair32(vmax(vmax(m0, st[0][15]), vmax(m1, st[1][15]))) * ts.cb;
+    rescale = __builtin_amdgcn_ballot_w64(mxs - ref8 > kRescaleLog2) != 0;
+    const float ref_use = rescale ? vmax(ref8, mxs) : ref8;
+    const float alpha = __builtin_amdgcn_exp2f(ref8 - ref_use);
+    ref8 = ref_use;
+    // mxs - ref_use <= kRescaleLog2 = 8 and log2 f < 1, so k >= -1 (2^-1 is an
+    // exact E8M0 factor too); a row with no key in the block (mxs = -inf)
+    // takes k = 64.
+    const float kf = fminf(8.0f - ceilf(mxs - ref_use + ts.lf), 64.0f);
     const int ki = (int)kf;
-    const float bias = fmaf(-m_use, c, kf);
+    const float bias = kf + ts.lf - ref_use;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[kt][i] = fmaf(st[kt][i], c, bias);
+      for (int i = 0; i < 16; ++i) st[kt][i] = fmaf(st[kt][i], ts.cb, bias);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -685,14 +726,14 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
       pw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(st[kt][4 * g + 2], st[kt][4 * g + 3], lo,
                                                         true);
     }
-    pw[8] = (uint32_t)(127 - ki);
+    pw[8] = (uint32_t)(127 - ki + ts.ev);
     float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) part[i % 4] += st[kt][i];
-    l_run = l_run * alpha +
-            __builtin_amdgcn_ldexpf((part[0] + part[1]) + (part[2] + part[3]), -ki);
+    const float ls = __builtin_amdgcn_ldexpf((part[0] + part[1]) + (part[2] + part[3]), -ki);
+    l_run = l_run * alpha + (KVT ? ls * ts.inv_f : ls);
     return alpha;
   };
 
@@ -754,7 +795,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     // The reference starts at the first block's max (every row has a key in
     // the first block of its range, so it is finite).
     if (needs_mask(kb_lo)) mask(sa, kb_lo * kBC);
-    ref_c = block_max(sa) * c;
+    ref_c = block_max(sa) * tile_scale(kb_lo).cb;
     barrier();
 
     constexpr int NPV = NDT * 4;     // P V MFMAs per block
@@ -766,15 +807,16 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
     // reference moves up to the block's max, O^T (which holds blocks up to
     // j - 1 once this iteration's P V has run) and l scale by
     // exp2(old - new), and P(j) is taken again.
-    auto rescale_block = [&](int j, const uint8_t* k_cur, f32x16* st, PRegs& p_cur) __attribute__((always_inline)) -> float {
+    auto rescale_block = [&](int j, const uint8_t* k_cur, f32x16* st, PRegs& p_cur,
+                             const TileScale& ts) __attribute__((always_inline)) -> float {
       qk(k_cur, st);  // into the registers of the block's spent fp32 probabilities
       mfma_read_pipeline<NQK, KCH, 1>();  // one operand read ahead: few registers in flight
       if (needs_mask(j)) mask(st, j * kBC);
-      const float ref_new = vmax(ref_c, block_max(st) * c);  // a fully masked row keeps ref_c
+      const float ref_new = vmax(ref_c, block_max(st) * ts.cb);  // a fully masked row keeps ref_c
       const float alpha = __builtin_amdgcn_exp2f(ref_c - ref_new);
       ref_c = ref_new;
-      const float ls = softmax(st, p_cur);
-      l_run = l_run * alpha + ls;
+      const float ls = softmax(st, p_cur, ts);
+      l_run = l_run * alpha + (KVT ? ls * ts.inv_f : ls);
       return alpha;
     };
     // One iteration as an explicit software pipeline of NM slices.  Slice m
@@ -797,6 +839,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
                     const uint8_t* v_prev, uint8_t* v_fill, f32x16* s_cur, f32x16* s_next,
                     PRegs& p_cur, const PRegs& p_prev) __attribute__((always_inline)) {
       if (needs_mask(j)) mask(s_cur, j * kBC);
+      const TileScale ts = tile_scale(j);
       uint32_t opnd[LA][OW];                       // operand ring, slot m % LA
       auto read = [&](auto mc) __attribute__((always_inline)) {
         constexpr int m = decltype(mc)::value;
@@ -832,14 +875,14 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
           s_next[kt] = mfma_qk<DT>(a, qreg[ks], ks == 0 ? f32x16{} : s_next[kt]);
         }
       };
-      const float nref = -ref_c;
+      const float nref = ts.lf - ref_c;
       float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
       auto softmax_slice = [&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          if (fma_slice(i) == k) s_cur[i / 16][i % 16] = fmaf(s_cur[i / 16][i % 16], c, nref);
+          if (fma_slice(i) == k) s_cur[i / 16][i % 16] = fmaf(s_cur[i / 16][i % 16], ts.cb, nref);
           if (fma_slice(i) + 1 == k) s_cur[i / 16][i % 16] = __builtin_amdgcn_exp2f(s_cur[i / 16][i % 16]);
           if (i % 2 == 1 && fma_slice(i) + 2 == k) {
             const int kt = i / 16, e = i % 16 - 1;
@@ -861,7 +904,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
         if constexpr (k < NM) mfma(kc);
         if constexpr (k + LA < NM) read(std::integral_constant<int, k + LA>{});
         softmax_slice(kc);
-        if constexpr (k == 0) store_v(vst, v_fill);            // V(j) -> V^T
+        if constexpr (k == 0) store_v(vst, v_fill, ts.vp2);    // V(j) -> V^T
         if constexpr (k == 2) load_v((j + 1) * kBC, vst);      // V(j+1) -> registers
         if constexpr (k == 4) load_k((j + 3) * kBC, k_fill);   // K(j+3), after V(j+1)
         __builtin_amdgcn_sched_barrier(0);
@@ -870,9 +913,9 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
       const bool big = __builtin_amdgcn_ballot_w64(!(ls < kRowSumCap)) != 0;
       float alpha = 1.0f;
       if (big) {
-        alpha = rescale_block(j, k_cur, s_cur, p_cur);
+        alpha = rescale_block(j, k_cur, s_cur, p_cur, ts);
       } else {
-        l_run += ls;
+        l_run += KVT ? ls * ts.inv_f : ls;
       }
       // O^T holds blocks up to j - 1 now (this iteration's P V has run), all
       // relative to the old reference.  (A branch of its own: inside the one
@@ -953,7 +996,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
       load_k((j + 3) * kBC, k_fill);    // K(j+3)
       pv8(v_prev, p_prev);              // P V of block j-1
       qk(k_next, s_next);               // QK^T of block j+1
-      alpha_prev = softmax8(s_cur, p_cur, resc_prev);
+      alpha_prev = softmax8(s_cur, p_cur, resc_prev, tile_scale(j));
       mfma_run_pipeline<NDT, 4, NQK, KCH, 2, VPM8, TPM8, 0, NVM8, VM08>();
       // Keep the whole run -- softmax, P V and QK^T MFMAs -- in this block:
       // the compiler would otherwise sink MFMAs past the barrier to their
@@ -1045,7 +1088,7 @@ __global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Para
       const u32x4 x = *reinterpret_cast<const u32x4*>(obuf + r * OROWB + ((ch ^ (r % OCH)) * 16));
       if (qw0 + r < N) *reinterpret_cast<u32x4*>(wrows + r * wstride + ch * 8) = x;
     }
-    const float ref_log2 = PV8 ? m_run * c : ref_c;
+    const float ref_log2 = PV8 ? ref8 : ref_c;
     if (hh == 0 && my_q < N) wlse[lr] = kLn2 * (ref_log2 + __builtin_amdgcn_logf(l_tot));
   }
 }
@@ -1175,7 +1218,7 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
 }
 
 // Query tiles [qt_lo, qt_hi) of every head (tiles of Shape<WAVES>::br rows).
-template <int DT, int D, bool CAUSAL, int WAVES, bool PV8 = false>
+template <int DT, int D, bool CAUSAL, int WAVES, bool PV8 = false, bool KVT = false>
 int launch_w(Params prm, int qt_lo, int qt_hi, hipStream_t stream) {
   using S = Shape<WAVES>;
   prm.qt_base = qt_lo;
@@ -1183,7 +1226,7 @@ int launch_w(Params prm, int qt_lo, int qt_hi, hipStream_t stream) {
   void* args[] = {&prm};
   const dim3 grid((unsigned)(prm.bh * prm.n_qtiles));
   hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, WAVES, PV8>), grid,
+      reinterpret_cast<const void*>(&fa_fwd_kernel<DT, D, CAUSAL, WAVES, PV8, KVT>), grid,
       dim3(S::threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -1218,7 +1261,7 @@ int launch_t(const Params& prm, int cus, hipStream_t stream) {
 // sees at least min_keys keys (causal: row i sees i + 1; otherwise all N), and
 // in fp16 for the tiles before: two launches over disjoint tiles, both with
 // 128-row tiles.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool KVT = false>
 int launch_pv8(const Params& prm, int64_t min_keys, hipStream_t stream) {
   constexpr int DT = FA_DTYPE_FP8_E4M3;
   constexpr int BR = Shape<4>::br;
@@ -1232,8 +1275,8 @@ int launch_pv8(const Params& prm, int64_t min_keys, hipStream_t stream) {
     n_lo = prm.N >= mk ? 0 : n_t;
   if (n_lo > n_t) n_lo = n_t;
   int st = FA_OK;
-  if (n_lo > 0) st = launch_w<DT, D, CAUSAL, 4, false>(prm, 0, n_lo, stream);
-  if (st == FA_OK && n_lo < n_t) st = launch_w<DT, D, CAUSAL, 4, true>(prm, n_lo, n_t, stream);
+  if (n_lo > 0) st = launch_w<DT, D, CAUSAL, 4, false, KVT>(prm, 0, n_lo, stream);
+  if (st == FA_OK && n_lo < n_t) st = launch_w<DT, D, CAUSAL, 4, true, KVT>(prm, n_lo, n_t, stream);
   return st;
 }
 
@@ -1414,10 +1457,13 @@ int launch_split_dt(const Params& prm, int d, int causal, const SplitPlan& pl, v
 // pv8_min_keys < 0: P V in fp16 throughout; otherwise (fp8 only) the split
 // of launch_pv8.  split: a plan with g > 0 runs the key-range split with
 // workspace ws.
+// kv_tiles: per-key-tile K / V scales (fp8 only, no split): P V in fp16
+// throughout when pv8_min_keys < 0, else as launch_pv8.
 int run(const void* q, const void* k, const void* v, const float* dq, const float* dk,
         const float* dv, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
         float scale, int causal, int dtype, int layout, void* stream,
-        int64_t pv8_min_keys = -1, const SplitPlan* split = nullptr, void* ws = nullptr) {
+        int64_t pv8_min_keys = -1, const SplitPlan* split = nullptr, void* ws = nullptr,
+        bool kv_tiles = false) {
   Params prm;
   prm.q = static_cast<const uint8_t*>(q);
   prm.k = static_cast<const uint8_t*>(k);
@@ -1438,9 +1484,27 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
   prm.split_cmax = 0;
   prm.ws_o = nullptr;
   prm.ws_lse = nullptr;
+  prm.n_kvt = (int)((N + kBC - 1) / kBC);
   const Topology topo = device_topology();
   prm.n_xcd = topo.xcds;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kv_tiles) {
+    constexpr int F8 = FA_DTYPE_FP8_E4M3;
+    if (pv8_min_keys >= 0) {
+      if (d == 64)
+        return causal ? launch_pv8<64, true, true>(prm, pv8_min_keys, s)
+                      : launch_pv8<64, false, true>(prm, pv8_min_keys, s);
+      return causal ? launch_pv8<128, true, true>(prm, pv8_min_keys, s)
+                    : launch_pv8<128, false, true>(prm, pv8_min_keys, s);
+    }
+    static_assert(default_waves<F8, 64>() == 4 && default_waves<F8, 128>() == 4, "fp8: 4 waves");
+    const int n64 = (int)((N + Shape<4>::br - 1) / Shape<4>::br);
+    if (d == 64)
+      return causal ? launch_w<F8, 64, true, 4, false, true>(prm, 0, n64, s)
+                    : launch_w<F8, 64, false, 4, false, true>(prm, 0, n64, s);
+    return causal ? launch_w<F8, 128, true, 4, false, true>(prm, 0, n64, s)
+                  : launch_w<F8, 128, false, 4, false, true>(prm, 0, n64, s);
+  }
   if (split && split->g > 0 && dtype == FA_DTYPE_FP8_E4M3 && pv8_min_keys >= 0) {
     if (d == 64)
       return causal ? launch_pv8_split<64, true>(prm, pv8_min_keys, *split, ws, s)
@@ -1560,6 +1624,23 @@ extern "C" int fa_fwd_fp8_pv(const void* q, const void* k, const void* v, const 
     return FA_ERR_ALIGN;
   return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal,
              FA_DTYPE_FP8_E4M3, layout, stream, min_keys);
+}
+
+extern "C" int fa_fwd_fp8_kvtile(const void* q, const void* k, const void* v,
+                                 const float* descale_q, const float* descale_k,
+                                 const float* descale_v, void* o, float* lse, int64_t B,
+                                 int64_t H, int64_t N, int64_t d, float scale, int causal,
+                                 int layout, int64_t pv_min_keys, void* stream) {
+  bool empty;
+  int st = check_args(q, k, v, o, lse, B, H, N, d, scale, causal, FA_DTYPE_FP8_E4M3, layout,
+                      &empty);
+  if (st != FA_OK || empty) return st;
+  if (!descale_q || !descale_k || !descale_v) return FA_ERR_NULL;
+  if (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4))
+    return FA_ERR_ALIGN;
+  return run(q, k, v, descale_q, descale_k, descale_v, o, lse, B, H, N, d, scale, causal,
+             FA_DTYPE_FP8_E4M3, layout, stream, pv_min_keys < 0 ? -1 : pv_min_keys, nullptr,
+             nullptr, true);
 }
 
 extern "C" int64_t fa_fwd_kvsplit_workspace(int64_t B, int64_t H, int64_t N, int64_t d,

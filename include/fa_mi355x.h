@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum {
   FA_DTYPE_FP16 = 0,      /* IEEE binary16 */
@@ -153,6 +153,36 @@ int fa_fwd_fp8_pv(const void* q, const void* k, const void* v,
                   const float* descale_v, void* o, float* lse,
                   int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                   int causal, int layout, int64_t min_keys, void* stream);
+
+/*
+ * fa_fwd_fp8_kvtile -- attention forward for OCP e4m3 inputs whose K and V
+ * carry one dequantization scale per tile of 64 consecutive key rows, the
+ * per-block scale of "第 17 章 TMA + Warp Specialization 把 FA2 写到 SOTA"
+ * (section 17.7, item 1: every K tile brings its own scale, so that one
+ * scale for the whole tensor does not cost precision), applied to V's rows
+ * in the same way.  Q keeps one scale per head.  With nt = ceil(N / 64):
+ *   q element (b, h, n, i) = e4m3 code * descale_q[b*H + h]
+ *   k element (b, h, n, i) = e4m3 code * descale_k[(b*H + h)*nt + n/64]
+ *   v element (b, h, n, i) = e4m3 code * descale_v[(b*H + h)*nt + n/64]
+ * descale_q: B*H floats; descale_k, descale_v: B*H*nt floats; all device
+ * arrays, required (FA_ERR_NULL), 4-byte aligned (FA_ERR_ALIGN), each a
+ * positive normal float (others give unspecified results; they are not
+ * read on the host); |V| must stay within the fp16 range.  O and LSE are
+ * those of the dequantized problem.  QK^T runs on the fp8 matrix
+ * instructions, each key tile's scale folded into that block's scores.
+ * pv_min_keys < 0: P V in fp16 (V's codes times the power-of-two part of
+ * its tile scale are exact in fp16; the rest of the scale multiplies the
+ * block's probabilities); pv_min_keys >= 0: P V on the fp8 matrix
+ * instructions for the query tiles fa_fwd_fp8_pv would put there (the tile
+ * scale's power of two travels in the instruction's block scale).  Other
+ * arguments as for fa_fwd_ex with dtype FA_DTYPE_FP8_E4M3.  One or two
+ * kernels are enqueued.  Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd_fp8_kvtile(const void* q, const void* k, const void* v,
+                      const float* descale_q, const float* descale_k,
+                      const float* descale_v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                      int causal, int layout, int64_t pv_min_keys, void* stream);
 
 /*
  * fa_fwd_kvsplit_workspace -- bytes of device workspace fa_fwd_kvsplit needs

@@ -377,3 +377,35 @@ def test_fa_fwd_kvsplit_noalloc_empty_is_a_noop():
 
 def test_noalloc_scratch_size():
     assert binding.kvsplit_noalloc_max_bytes() == 64 << 20
+
+
+def _call_kvtile(**kw):
+    lib = binding.load_library()
+    args = dict(q=Q, k=K, v=V, dq=A + 0x5000, dk=A + 0x6000, dv=A + 0x7000, o=O, lse=L, B=1,
+                H=2, N=300, d=128, scale=0.1, causal=1, layout=0, min_keys=-1, stream=None)
+    args.update(kw)
+    return lib.fa_fwd_fp8_kvtile(args["q"], args["k"], args["v"], args["dq"], args["dk"],
+                                 args["dv"], args["o"], args["lse"], args["B"], args["H"],
+                                 args["N"], args["d"], args["scale"], args["causal"],
+                                 args["layout"], args["min_keys"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=None), "FA_ERR_NULL"),
+    (dict(dk=None), "FA_ERR_NULL"),
+    (dict(dv=None), "FA_ERR_NULL"),
+    (dict(dk=A + 0x6002), "FA_ERR_ALIGN"),
+    (dict(layout=3), "FA_ERR_LAYOUT"),
+    (dict(d=32), "FA_ERR_HEAD_DIM"),
+    (dict(causal=2), "FA_ERR_CAUSAL"),
+    (dict(scale=float("inf")), "FA_ERR_SCALE"),
+    (dict(lse=None), "FA_ERR_NULL"),
+    (dict(o=O + 4), "FA_ERR_ALIGN"),
+])
+def test_fa_fwd_fp8_kvtile_rejects(kw, status):
+    assert _call_kvtile(**kw) == _header_constants()[status]
+
+
+def test_fa_fwd_fp8_kvtile_empty_is_a_noop():
+    assert _call_kvtile(N=0, q=None, k=None, v=None, o=None, lse=None, dq=None, dk=None,
+                        dv=None) == 0

@@ -26,7 +26,7 @@ import torch
 
 from attention_forward_fa_amd import binding, inputs
 from oracle import attention as oracle
-from tests.test_gpu_parity import _sample_rows, announce, check, to_np
+from tests.test_gpu_parity import _sample_rows, announce, check, fp8_dot_err, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -65,17 +65,21 @@ def abs_v(inp):
                              inp.descale_k, inp.descale_v, inp.seed)
 
 
-def check_e4m3_bound(inp, o, l, heads=None, rows=None, lse_tol=1e-3):
+def check_e4m3_bound(inp, o, l, heads=None, rows=None):
+    # The fp8 dot error on the scores (E_i per row, see test_gpu_parity) moves
+    # the weights by at most 2 E_i relative and LSE by E_i.
     o_ref, l_ref = oracle.run(inp, rows=rows, heads=heads)
     a_ref, _ = oracle.run(abs_v(inp), rows=rows, heads=heads)
     hsel = np.arange(inp.B * inp.H) if heads is None else np.asarray(heads)
     rsel = np.arange(inp.N) if rows is None else np.asarray(rows)
+    e = fp8_dot_err(inp, hsel, rsel)[:, :, None]
+    lse_tol = 1e-3 + e[:, :, 0]
     og, lg = o[hsel][:, rsel], l[hsel][:, rsel]
     assert np.isfinite(og).all() and np.isfinite(lg).all(), inp.describe()
     v = torch.from_numpy(inp.v).view(torch.float8_e4m3fn).double().numpy()
     v = v.reshape(inp.B * inp.H, inp.N, inp.d) * inp.descale_v.astype(np.float64)[:, None, None]
     vmax = np.abs(v[hsel]).max(axis=1)[:, None, :]  # per head and column
-    bound = 2.0 ** -4 * a_ref + 63 * 2.0 ** -17 * vmax + 4e-3
+    bound = (2.0 ** -4 + 2 * e) * a_ref + 63 * 2.0 ** -17 * vmax + 4e-3
     d_o = np.abs(og - o_ref)
     d_l = np.abs(lg - l_ref)
     ratio = float((d_o / bound).max())
@@ -89,7 +93,7 @@ def check_e4m3_bound(inp, o, l, heads=None, rows=None, lse_tol=1e-3):
                                 "max_dO_over_bound": ratio, "max_dLSE": float(d_l.max()),
                                 "rows": int(len(rsel)), "heads": int(len(hsel))}) + "\n")
     assert ratio <= 1.0, inp.describe()
-    assert d_l.max() <= lse_tol, inp.describe()
+    assert (d_l <= lse_tol).all(), inp.describe()
     return d_o
 
 
@@ -193,12 +197,12 @@ def test_zero_q_gives_lse_of_uniform_rows():
 
 
 def test_large_scores():
-    # Scores of order 100 (past fp32 exp overflow): LSE bar relative to |LSE|
-    # as in the other parity tests.
+    # Scores of order 100 (past fp32 exp overflow), with the fp8 dot error of
+    # such scores in the bars.
     inp = inputs.draw(1, 2, 700, 64, "fp8", False, seed=1800, scale=4.0)
     o, l = to_np(*run_pv(inp, min_keys=0), inp)
     assert float(np.abs(l).max()) > 88.0
-    check_e4m3_bound(inp, o, l, lse_tol=1e-3 + 1e-4 * float(np.abs(l).max()))
+    check_e4m3_bound(inp, o, l)
 
 
 def test_config5_full_size_sampled():

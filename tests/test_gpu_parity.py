@@ -2,7 +2,13 @@
 
 Bars (absolute, element-wise, O upcast to float64 against the oracle's exact O):
   fp16 / bf16:  max|dO| <= 4e-3, mean|dO| <= 5e-4, max|dLSE| <= 1e-3
-  fp8 (e4m3):   max|dO| <= 3e-2, mean|dO| <= 3.75e-3, max|dLSE| <= 1e-3
+  fp8 (e4m3):   max|dO| <= 3e-2, mean|dO| <= 3.75e-3,
+                |dLSE_i| <= 1e-3 + 2^-12 * max_j scale * sum_c |q_ic| |k_jc|
+The fp8 LSE bar adds the fp8 matrix instruction's own dot-product error: it
+sums its products with an error of up to 2^-12.4 of the sum of their
+magnitudes (test_gpu_dot_precision measures it through causal row 0, whose
+LSE is one score), where the fp16 and bf16 instructions are exact to fp32
+rounding.  A row's LSE moves by at most its largest score error.
 """
 import json
 import os
@@ -45,6 +51,27 @@ def to_np(o, l, inp):
     return o, l
 
 
+FP8_DOT_REL = 2.0 ** -12  # fp8 matrix-instruction dot error / sum of |products| (measured <= 2^-12.4)
+
+
+def fp8_dot_err(inp, heads, rows):
+    """Largest fp8 score error of each row [len(heads), len(rows)]: FP8_DOT_REL
+    times the row's largest sum of product magnitudes over the keys it sees."""
+    out = []
+    for f in heads:
+        q, k, _ = oracle.head_values(inp, int(f) // inp.H, int(f) % inp.H)
+        mag = float(inp.scale) * (np.abs(q[rows]) @ np.abs(k).T)
+        if inp.causal:
+            mag = np.where(np.arange(inp.N)[None, :] <= np.asarray(rows)[:, None], mag, 0.0)
+        out.append(FP8_DOT_REL * mag.max(axis=1))
+    return np.stack(out)
+
+
+def fp8_lse_bar(inp, heads, rows):
+    """Per-row fp8 LSE bar: 1e-3 plus the row's largest score error."""
+    return 1e-3 + fp8_dot_err(inp, heads, rows)
+
+
 def check(inp, o, l, heads=None, rows=None, tol=None):
     o_ref, l_ref = oracle.run(inp, rows=rows, heads=heads)
     hsel = np.arange(inp.B * inp.H) if heads is None else np.asarray(heads)
@@ -53,6 +80,8 @@ def check(inp, o, l, heads=None, rows=None, tol=None):
     lg = l[hsel][:, rsel]
     assert np.isfinite(og).all() and np.isfinite(lg).all(), inp.describe()
     mx_o, mean_o, mx_l = tol or TOL[inp.dtype]
+    if inp.dtype == "fp8" and tol is None:
+        mx_l = fp8_lse_bar(inp, hsel, rsel)
     d_o = np.abs(og - o_ref)
     d_l = np.abs(lg - l_ref)
     msg = (f"{inp.describe()}: max|dO|={d_o.max():.3e} mean|dO|={d_o.mean():.3e} "
@@ -66,7 +95,7 @@ def check(inp, o, l, heads=None, rows=None, tol=None):
                                 "rows": int(len(rsel)), "heads": int(len(hsel))}) + "\n")
     assert d_o.max() <= mx_o, msg
     assert d_o.mean() <= mean_o, msg
-    assert d_l.max() <= mx_l, msg
+    assert (d_l <= mx_l).all(), msg
     return d_o.max(), d_o.mean(), d_l.max()
 
 
@@ -187,18 +216,24 @@ def test_causal_row0_is_v0_exactly(dtype, d):
 def test_large_scores(dtype):
     # Scores of order 100 (beyond fp32 exp overflow at ~88): the running max
     # must be subtracted before exp.  fp16 / bf16 keep the absolute bars.
+    # fp8 takes its derived LSE bar (check's default).
     inp = inputs.draw(1, 2, 130, 64, dtype, False, seed=24, scale=4.0)
     o, l = to_np(*gpu_run(inp), inp)
     assert float(np.abs(l).max()) > 88.0
-    tol = None
-    if dtype == "fp8":
-        tol = (TOL[dtype][0], TOL[dtype][1], 1e-3 + 1e-4 * float(np.abs(l).max()))
-    check(inp, o, l, tol=tol)
+    check(inp, o, l)
 
 
 def test_fp8_unit_descale_entry_point():
-    # fa_fwd with dtype FP8 = codes taken at unit scale.
-    # Codes reach |448| at unit scale; a small softmax scale keeps scores moderate.
+    # fa_fwd with dtype FP8 takes the codes at unit scale, so values reach 448
+    # and the fixed bars (made for N(0, 1) data) do not apply.  Bars derived
+    # for this problem, per element: fp16 rounding of each probability
+    # (relative 2^-11; the row sum sums the same rounded values, so the
+    # weights move by at most 2^-10 relative) spreads O by at most
+    # 2^-10 sum_j w_ij |v_jc - O_ic|; the fp8 dot error E_i (each score within
+    # 2^-12 scale max_j sum_c |q_ic k_jc|) moves the weights by at most 2 E_i
+    # relative; O's fp16 rounding adds 2^-11 |O_ic|; probabilities below the
+    # fp16 normal range lose at most 2^-25 each against a row sum >= 1.
+    # LSE: 2^-11 (row sum of rounded values) + E_i + fp32 rounding.
     inp = inputs.draw(1, 2, 190, 128, "fp8", True, seed=25, scale=1e-4)
     q, k, v, _ = binding.to_device(inp)
     announce("fa_fwd fp8 unit descale " + inp.describe())
@@ -208,8 +243,22 @@ def test_fp8_unit_descale_entry_point():
     ref_inp = inputs.AttnInputs(inp.B, inp.H, inp.N, inp.d, "fp8", True, inp.scale, inp.q,
                                 inp.k, inp.v, unit, unit, unit)
     on, ln = to_np(o, l, inp)
-    # Unit-scale codes reach |v| = 448: the O bar scales with the value range.
-    check(ref_inp, on, ln, tol=(3e-2 * 448 / 4, 3.75e-3 * 448 / 4, 1e-3 * 30))
+    o_ref, l_ref = oracle.run(ref_inp)
+    for f in range(inp.B * inp.H):
+        qv, kv, vv = oracle.head_values(ref_inp, f // inp.H, f % inp.H)
+        w = oracle.attention_probs(qv, kv, inp.scale, True)
+        mag = np.where(np.tri(inp.N, dtype=bool), inp.scale * (np.abs(qv) @ np.abs(kv).T), 0.0)
+        e = 2.0 ** -12 * mag.max(axis=1)
+        dev = np.abs(vv[None, :, :] - o_ref[f][:, None, :])  # [i, j, c] = |v_jc - O_ic|
+        spread = np.einsum("ij,ijc->ic", w, dev)
+        bound = ((2.0 ** -10 + 2 * e[:, None]) * spread + 2.0 ** -11 * np.abs(o_ref[f])
+                 + inp.N * 2.0 ** -25 * dev.max(axis=1) + 1e-6)
+        d_o = np.abs(on[f] - o_ref[f])
+        d_l = np.abs(ln[f] - l_ref[f])
+        announce(f"head {f}: max|dO|={d_o.max():.3e} max|dO|/bound={(d_o / bound).max():.3f} "
+                 f"max|dLSE|={d_l.max():.3e}")
+        assert (d_o <= bound).all(), float((d_o / bound).max())
+        assert (d_l <= 2.0 ** -11 + e + 1e-5).all(), float(d_l.max())
 
 
 def test_many_heads_distinct():

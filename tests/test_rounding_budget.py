@@ -110,3 +110,48 @@ def test_fp8_probabilities_need_512_keys():
     assert err[("short", False)] <= 4e-3 and err[("long", False)] <= 4e-3, err
     assert err[("short", True)] > 3e-2, err      # e4m3 P alone misses the bar on short rows
     assert err[("long", True)] <= 2e-2, err      # and meets it from 512 keys on
+
+
+# --- fp8 scores: what accumulation precision the LSE of large scores needs ---
+
+def _aligned_sum(prod, bits):
+    """Sum of each row's products (last axis) after truncating every product
+    toward zero to a multiple of 2^(E - bits), E the binade of the row's
+    largest product: an accumulator that aligns its inputs to the largest
+    one and keeps `bits` fraction bits."""
+    mx = np.abs(prod).max(axis=-1, keepdims=True)
+    e = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
+    unit = np.exp2(e - bits)
+    return (np.trunc(prod / unit) * unit).sum(axis=-1)
+
+
+def _lse_from_raw(raw, c_nat):
+    s = raw * c_nat
+    m = s.max(axis=1, keepdims=True)
+    return (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+
+
+def test_fp8_large_score_lse_needs_the_instruction_precision():
+    # The fp8 large-score case (scale 4, scores of order 100).  Products of
+    # two e4m3 codes are exact; summed with fp32 rounding after every
+    # addition they leave LSE within 1e-4 of the exact value, so fp32
+    # arithmetic cannot produce errors near 1e-3.  An accumulator that aligns
+    # the 64 products of one instruction to the largest and keeps 12 fraction
+    # bits gives errors of that order -- the relative error 2^-12 of the
+    # magnitude sum that test_gpu_dot_precision bounds on the GPU and that
+    # the fp8 LSE bars allow for -- and stays inside that bar.
+    inp = inputs.draw(1, 2, 130, 64, "fp8", False, seed=24, scale=4.0)
+    Q, K = _codes(inp.q)[0], _codes(inp.k)[0]
+    for h in range(inp.H):
+        c_nat = inp.scale * float(inp.descale_q[h]) * float(inp.descale_k[h])
+        prod = Q[h][:, None, :] * K[h][None, :, :]          # [i, j, c], exact
+        exact = _lse_from_raw(prod.sum(axis=-1), c_nat)
+        acc = np.zeros(prod.shape[:2], dtype=np.float32)
+        for cidx in range(prod.shape[2]):                   # fp32 after every add
+            acc = (acc + prod[:, :, cidx].astype(np.float32)).astype(np.float32)
+        fp32_err = np.abs(_lse_from_raw(acc.astype(np.float64), c_nat) - exact).max()
+        assert fp32_err < 1e-4, fp32_err
+        bar = 2.0 ** -12 * c_nat * np.abs(prod).sum(axis=-1).max(axis=1)
+        assert bar.max() > 1e-2  # scores this large allow more than 1e-3
+        err12 = np.abs(_lse_from_raw(_aligned_sum(prod, 12), c_nat) - exact)
+        assert 1e-4 < err12.max() and (err12 <= bar).all(), (err12.max(), bar.min())
