@@ -61,6 +61,9 @@ def parse_args(argv=None):
                     help="fp8 workloads: P V on the fp8 matrix instructions as well "
                          "(fa_fwd_fp8_pv) for query tiles whose first row sees at least "
                          "MIN_KEYS keys (512 keeps the fp8 error bars)")
+    ap.add_argument("--kv-tile", action="store_true",
+                    help="fp8 workloads: K and V quantized per 64-row key tile, run "
+                         "fa_fwd_fp8_kvtile (P V in fp16, or as --fp8-pv says)")
     ap.add_argument("--kvsplit", action="store_true",
                     help="run fa_fwd_kvsplit (key ranges of long query tiles split over "
                          "workgroups and merged; workspace allocated before timing)")
@@ -194,7 +197,11 @@ def fwd_step(inp, layout="bhnd", pv8=None, kvsplit=False):
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def step():
-        if kvsplit and pv8 is not None and inp.dtype == "fp8":
+        if inp.dtype == "fp8" and inp.kv_tile:
+            binding.fwd_fp8_kvtile(q, k, v, ds, pv_min_keys=-1 if pv8 is None else pv8,
+                                   layout=layout, causal=inp.causal, scale=inp.scale,
+                                   out=out, lse=lse)
+        elif kvsplit and pv8 is not None and inp.dtype == "fp8":
             binding.fwd_fp8_pv_kvsplit(q, k, v, min_keys=pv8, layout=layout, causal=inp.causal,
                                        scale=inp.scale, descales=ds, out=out, lse=lse,
                                        workspace=ws)
@@ -341,7 +348,10 @@ def main(argv=None):
             raise SystemExit("the backward pass takes fp16 or bf16 workloads")
         inp = inputs.draw_bwd(B, H, N, d, dtype, causal, seed)
     else:
-        inp = inputs.draw(B, H, N, d, dtype, causal, seed)
+        if args.kv_tile and dtype != "fp8":
+            raise SystemExit("--kv-tile takes fp8 workloads")
+        inp = inputs.draw(B, H, N, d, dtype, causal, seed,
+                          kv_tile=64 if args.kv_tile else None)
     timing = dict(steps=args.steps, warmup=args.warmup, reps=args.reps, settle_s=args.settle_s)
     if args.which == "bwd":
         # Backward pass: 5 products of 2*N^2*d per head (2.5x the forward count).
@@ -412,7 +422,9 @@ def main(argv=None):
                    "outputs": "O fp16 + LSE fp32", "accumulate": "fp32",
                    **({"pv": f"fp8 from min_keys={args.fp8_pv}"}
                       if args.fp8_pv is not None and dtype == "fp8" else {}),
-                   **({"kvsplit": True} if args.kvsplit else {})},
+                   **({"kvsplit": True} if args.kvsplit else {}),
+                   **({"kv_tile": 64, "descales": "K, V per 64-row tile; Q per head"}
+                      if args.kv_tile else {})},
         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tf / peak, 4),
                      "traffic": measured_traffic(name, args.layout)},
