@@ -102,6 +102,12 @@ struct Shape {
 };
 constexpr int kMinBR = kQW * 4;           // smallest query tile of any kernel
 
+// Workgroups a CU must hold at once (the register budget follows): two
+// (two waves per SIMD), or three for the 4-wave d = 64 kernels, whose 50 KiB
+// of LDS leave room for a third workgroup when the registers allow it.
+template <int D, int WAVES>
+constexpr int min_wgs_per_cu() { return (D == 64 && WAVES == 4) ? 3 : 2; }
+
 template <int DT>
 __device__ __forceinline__ f32x16 mfma_qk(const QKOperand<DT>& a, const QKOperand<DT>& b,
                                           f32x16 c) {
@@ -250,7 +256,8 @@ __device__ __forceinline__ int vswz8(int row) {
 // runs in fp16.  KVT: fp8 with K and V dequantization scales per key tile
 // (one per block of kBC keys) instead of per head.
 template <int DT, int D, bool CAUSAL, int WAVES, bool PV8 = false, bool KVT = false>
-__global__ __launch_bounds__((Shape<WAVES>::threads), 2) void fa_fwd_kernel(Params p) {
+__global__ __launch_bounds__((Shape<WAVES>::threads), (min_wgs_per_cu<D, WAVES>()))
+void fa_fwd_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int kWaves = Shape<WAVES>::waves;
   constexpr int kThreads = Shape<WAVES>::threads;
