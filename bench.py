@@ -70,6 +70,9 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip reading the graphics clock after the timed windows (its ~1 s "
+                         "of extra launches swamps a counter-collection run)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every workload and print one line each to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -385,7 +388,8 @@ def main(argv=None):
     step = fwd_step(inp, args.layout, args.fp8_pv, args.kvsplit)
     windows, settled = timed_windows(step, **timing)
     sec = statistics.median(windows)
-    clock.mhz = clock.run(step, 1.0)
+    if not args.no_clock:
+        clock.mhz = clock.run(step, 1.0)
     flops, tf, peak = describe(inp, sec)
     if args.sweep:
         for cfg in inputs.CONFIGS + inputs.EXTRA_WORKLOADS + inputs.SHARD_WORKLOADS:
