@@ -358,8 +358,12 @@ def main(argv=None):
     timing = dict(steps=args.steps, warmup=args.warmup, reps=args.reps, settle_s=args.settle_s)
     if args.which == "bwd":
         # Backward pass: 5 products of 2*N^2*d per head (2.5x the forward count).
-        windows, settled = timed_windows(bwd_step(inp), **timing)
+        step = bwd_step(inp)
+        windows, settled = timed_windows(step, **timing)
         sec = statistics.median(windows)
+        clock = ClockSampler()
+        if not args.no_clock:
+            clock.mhz = clock.run(step, 1.0)
         flops = 2.5 * acc.counted_flops(B, H, N, d, causal)
         tf = flops / sec / 1e12
         peak = acc.PEAK_TFLOPS[dtype]
@@ -379,6 +383,8 @@ def main(argv=None):
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
                          "scope": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel"},
+            "clock": {"sclk_mhz": round(clock.mhz, 1) if clock.mhz else None,
+                      "samples": len(clock.samples)},
         }
         if not args.no_cpu_baseline:
             rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, "bwd")
