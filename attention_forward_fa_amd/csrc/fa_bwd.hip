@@ -19,14 +19,15 @@
 //     64-query block, dV^T += dO^T P, and passes P through LDS to the dS wave,
 //     which holds the V rows, computes dP = dO V^T, dS = P (dP - D) and
 //     dK^T += Q^T dS; dO^T / Q^T are read transposed from the row-major
-//     dO / Q blocks.
+//     dO / Q blocks.  Each wave's step is a software pipeline: the second
+//     product of one block runs beside the elementwise work of the next.
 // Blocks stream global -> LDS (buffer_load ... lds, XOR-swizzled 16-byte
 // chunks), one barrier per block: the dQ kernel double-buffers K and V and
 // unrolls its loop by two (running to an even block count, the extra block
-// fully masked); the dK/dV kernel keeps three Q stages and two dO stages and
-// unrolls by six, leaving after the last block.  Every stage index is thus a
-// constant.  Rows past N read as zeros and are masked, as are causal pairs
-// (key j > query i).  P and dS enter the second products
+// fully masked); the dK/dV kernel keeps four Q stages and two dO stages and
+// unrolls by four (running to a multiple of four blocks, the extra blocks
+// zero).  Every stage index is thus a constant.  Rows past N read as zeros
+// and are masked, as are causal pairs (key j > query i).  P and dS enter the second products
 // in the input type (fp16 or bf16, round to nearest even); the dK kernel's dS
 // is formed from that rounded P, the dQ kernel's from P in fp32.  All
 // accumulation is fp32 and the gradients are stored as fp32.
@@ -382,14 +383,27 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
 // computes dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS.  Four products per
 // block, where a dV pass and a dK pass of their own would take five (S twice);
 // each wave holds one key operand and one accumulator, so all eight fit two
-// waves per SIMD, and the two kinds' VALU work lands in different halves of
-// the block, beside the other kind's matrix instructions.
+// waves per SIMD (one of each kind), and each kind's elementwise work issues
+// beside the matrix instructions of its own second product and of the other
+// kind's wave on the SIMD.
 // ---------------------------------------------------------------------------
 constexpr int kKVWaves = 2 * kBwdWaves;  // waves 0-3: P, 4-7: dS, of key group wave % 4
 constexpr int kKVThreads = kWave * kKVWaves;
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Slice of the dK/dV step in which element e (0 .. 31; accumulator e / 16,
+// element e % 16) of the first product gets its first elementwise operation.
+// The run is 2 NKS first-product matrix instructions, accumulator 0's chain
+// first, then NM - 2 NKS second-product ones: accumulator 0's elements start
+// two slices after its chain's last instruction, accumulator 1's likewise, and
+// the last element leaves two slices for its remaining operations.
+template <int NKS, int NM>
+constexpr int bwd_vslice(int e) {
+  constexpr int R0 = NKS + 1, R1 = 2 * NKS + 1, RL = NM - 2;
+  return e < 16 ? R0 + (e * (R1 - R0)) / 16 : R1 + ((e - 16) * (RL - R1 + 1)) / 16;
 }
 
 template <int DT, int D, bool CAUSAL>
@@ -399,23 +413,39 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
   constexpr int NDT = D / 32;
   constexpr int BLK = kBS * ROWB;
   constexpr int PBLK = kRW * kBS * 2;  // one group's P block in the input type
-  // The P waves run one query block ahead of the dS waves: in step j a P
-  // wave computes P of block j + 1 (from Q_{j+1}) and dV of block j, its dS
-  // wave dS and dK of block j (from P_j, dO_j, Q_j), while Q_{j+2} and
-  // dO_{j+1} stream in -- three Q stages, two dO stages, one barrier a step.
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[3][BLK];
-  __shared__ __attribute__((aligned(16))) uint8_t do_lds[2][BLK];
-  // LSE (times log2 e) and D of a block's 64 queries.
-  __shared__ __attribute__((aligned(16))) float lse_lds[2][kBS];
-  __shared__ __attribute__((aligned(16))) float d_lds[2][kBS];
-  // P of each key group, from its P wave to its dS wave: lane l's 16 dwords
-  // as four 16-byte pieces at (c * 64 + l) * 16, c = 0 .. 3.
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][kBwdWaves][PBLK];
+  // Step j of the loop, in each 32-key group:
+  //   P wave:  S(j+1) = Q(j+1) K^T, then dV^T += dO(j)^T P(j) with P(j) in
+  //            registers since step j-1, while the exponentials of S(j+1)
+  //            run beside those matrix instructions; P(j+1) goes to LDS.
+  //   dS wave: dP(j) = dO(j) V^T, then dK^T += Q(j-1)^T dS(j-1) with dS(j-1)
+  //            in registers since step j-1, while dS(j) = P(j) (dP(j) - D(j))
+  //            is formed beside them from the P(j) its P wave stored.
+  // Meanwhile Q(j+2) and dO(j+1) stream in.  Q is read as Q(j+1) and Q(j-1)
+  // and loaded as Q(j+2): four stages; dO, P, LSE and D two each.  One
+  // barrier a step.
+  //
+  // LDS, one buffer: Q stages, dO stages, P (per stage and key group: lane
+  // l's 16 dwords as four 16-byte pieces at (c * 64 + l) * 16, c = 0 .. 3),
+  // LSE (times log2 e; +inf for rows at or past N) and D of a block's 64
+  // queries.  Every access in the loop is a per-lane base register plus an
+  // immediate offset (16 bits): each wave keeps one base into the Q or dO
+  // stages for its row-wise reads and one into the other for its transposed
+  // reads, so no stage needs registers of its own.
+  constexpr int OFF_Q = 0;
+  constexpr int OFF_DO = OFF_Q + 4 * BLK;
+  constexpr int OFF_P = OFF_DO + 2 * BLK;
+  constexpr int PSTAGE = kBwdWaves * PBLK;
+  constexpr int OFF_LSE = OFF_P + 2 * PSTAGE;
+  constexpr int OFF_D = OFF_LSE + 2 * kBS * 4;
+  constexpr int LDS_BYTES = OFF_D + 2 * kBS * 4;
+  static_assert(3 * BLK + 3 * 16 * ROWB <= 65535 && PSTAGE + 3 * 1024 <= 65535,
+                "immediate offsets must fit 16 bits");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lr = lane & 31, hh = lane >> 5;
+  const int hh = lane >> 5;
   const bool pw = wave < kBwdWaves;  // P wave, else dS wave (wave-uniform)
   const int grp = wave % kBwdWaves;
 
@@ -436,7 +466,7 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
       reinterpret_cast<const uint8_t*>(p.delta + (int64_t)bh * N), N * 4);
 
   const int k0 = kt * kBT;
-  const int my_k = k0 + grp * kRW + lr;
+  const int my_k = k0 + grp * kRW + (lane & 31);
   const float cs = p.scale * kLog2e;
 
   // This lane's key row of K (P wave) or V (dS wave): the B operand of
@@ -450,6 +480,45 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
   qa.init(lane);
   BlockLoader<ROWB, kKVWaves> ld;
   ld.init(wave, lane);
+  // Per-lane LDS bases (opaque to the compiler, so that it keeps one register
+  // each instead of one per stage): row-wise reads of the first product's A
+  // block (Q for a P wave, dO for a dS wave), transposed reads of the second
+  // product's block (dO, Q), this lane's P pieces, and the per-row values
+  // (LSE for a P wave, D for a dS wave) at this lane's half.
+  uint32_t arow[NKS], atr[NDT][2];
+  const uint32_t a_win = pw ? OFF_Q : OFF_DO, t_win = pw ? OFF_DO : OFF_Q;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    arow[ks] = qa.row[ks] + a_win;
+    asm volatile("" : "+v"(arow[ks]));
+  }
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      atr[t][h] = qa.tr[t][h] + t_win;
+      asm volatile("" : "+v"(atr[t][h]));
+    }
+  uint32_t pbase = OFF_P + grp * PBLK + lane * 16;
+  uint32_t rbase = (pw ? OFF_LSE : OFF_D) + 16 * hh;
+  asm volatile("" : "+v"(pbase), "+v"(rbase));
+  auto lds16 = [&](uint32_t base, int off) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4*>(smem + base + off);
+  };
+  // A operand at row tile t2, k-step ks of the block at byte `stage` of the
+  // A window; transposed operand (d tile t, 16-row group g) likewise.
+  auto a_read = [&](int stage, int t2, int ks) __attribute__((always_inline)) {
+    return lds16(arow[ks], stage + t2 * 32 * ROWB);
+  };
+  auto t_read = [&](int stage, int t, int g) __attribute__((always_inline)) {
+    const int off = stage + g * 16 * ROWB;
+    short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4_t_bwd*)(smem + atr[t][0] + off));
+    short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4_t_bwd*)(smem + atr[t][1] + off));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
 
   // Query blocks that can see a key of this tile: all, or (causal) from the
   // block holding query k0 on.
@@ -463,179 +532,270 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
 
   // LSE and D rows of a block, one dword per lane: D goes straight to LDS
   // (wave 1); LSE passes through wave 0's registers to be stored already
-  // multiplied by log2 e, once per row instead of once per score.
+  // multiplied by log2 e, once per row instead of once per score.  A row at
+  // or past N stores +inf, so that its probabilities come out 0 without a
+  // mask.
   float lse_next = 0.0f;
   auto load_lse = [&](int row0) __attribute__((always_inline)) {
     const int off = (row0 < N ? row0 : N) * 4 + lane * 4;  // past N: zeros
     if (wave == 0) lse_next = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, off, 0, 0));
   };
-  auto store_lse = [&](float* lse_dst) __attribute__((always_inline)) {
-    if (wave == 0) lse_dst[lane] = lse_next * kLog2e;
+  auto store_lse = [&](int stage, int row0) __attribute__((always_inline)) {
+    if (wave == 0)
+      reinterpret_cast<float*>(smem + OFF_LSE + stage * kBS * 4)[lane] =
+          row0 + lane < N ? lse_next * kLog2e : __builtin_inff();
   };
-  auto load_d = [&](float* d_dst, int row0) __attribute__((always_inline)) {
+  auto load_d = [&](int stage, int row0) __attribute__((always_inline)) {
     const int off = (row0 < N ? row0 : N) * 4 + lane * 4;
-    if (wave == 1) buffer_to_lds4(drs, d_dst, off);
+    if (wave == 1) buffer_to_lds4(drs, smem + OFF_D + stage * kBS * 4, off);
+  };
+  auto load_q = [&](int stage, int row0) __attribute__((always_inline)) {
+    ld.load(qrs, smem + OFF_Q + stage * BLK, row0, N);
+  };
+  auto load_do = [&](int stage, int row0) __attribute__((always_inline)) {
+    ld.load(dors, smem + OFF_DO + stage * BLK, row0, N);
   };
 
-  // P of block j (P wave): S = Q K^T from Q block qb, exp2 against the
-  // block's LSE, masked pairs 0, as pairs of the input type in w.  Elements
-  // 4 g .. 4 g + 3 of tile t2 are query rows t2*32 + 8 g + 4 hh .. +3, whose
-  // LSE log2 e (and D) are four consecutive floats; they go to k-step g / 2,
-  // dwords 2 (g % 2), +1.  The P goes to LDS at px, for the dS wave and for
-  // the P wave's own dV product a step later.
-  auto p_block = [&](int j, const uint8_t* qb, const float* lb, uint8_t* px)
-      __attribute__((always_inline)) {
-    const int qrow0 = row0_of(j);
-    uint32_t w[2][2][4];
+  // Element e (0 .. 15) of accumulator t2 is query row t2*32 + 8*(e/4) +
+  // 4*hh + e%4 of the block; its pair (e, e+1), e even, is dword
+  // w[t2][e/8][(e%8)/2] of the block's P or dS registers -- the order in which
+  // the 32x32 MFMA takes its B operand for the second products.
+  using BRegs = uint32_t[2][2][4];
+  auto brow = [&](int t2, int e) { return t2 * 32 + 8 * (e / 4) + 4 * hh + e % 4; };
+  // Zeroes the probabilities of causally masked pairs (query before key) in
+  // the block starting at query qrow0.
+  auto causal_mask = [&](BRegs& w, int qrow0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const int qi = qrow0 + brow(t2, e);  // rows qi, qi + 1
+        const uint32_t m = (qi >= my_k ? 0xffffu : 0u) | (qi + 1 >= my_k ? 0xffff0000u : 0u);
+        w[t2][e / 8][(e % 8) / 2] &= m;
+      }
+  };
+  auto store_b = [&](int stage, const BRegs& w) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<u32x4*>(smem + pbase + stage * PSTAGE + c * kWave * 16) =
+          u32x4{w[c / 2][c % 2][0], w[c / 2][c % 2][1], w[c / 2][c % 2][2], w[c / 2][c % 2][3]};
+  };
+  auto load_b = [&](int stage, BRegs& w) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 pv = lds16(pbase, stage * PSTAGE + c * kWave * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[c / 2][c % 2][e] = pv[e];
+    }
+  };
+
+  // Block 0's P (P waves), before the loop: S = Q K^T, then P with the
+  // causal mask, to LDS and into w.
+  auto first_p = [&](BRegs& w) __attribute__((always_inline)) {
     f32x16 x[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) x[t2] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-        x[t2] = mfma16<DT>(row_operand<ROWB>(qb, qa, t2, ks), kv[ks], x[t2]);
+      for (int t2 = 0; t2 < 2; ++t2) x[t2] = mfma16<DT>(a_read(0, t2, ks), kv[ks], x[t2]);
     mfma_read_pipeline<2 * NKS, 1, 4>();
     __builtin_amdgcn_sched_barrier(0);
-    // Only a block reaching past N or below the tile's last key needs the
-    // mask (a uniform branch; exp2 of a masked score is replaced, never used).
-    const bool edge = qrow0 + kBS > N || (CAUSAL && qrow0 < k0 + kBT);
+    const float* lb = reinterpret_cast<const float*>(smem + OFF_LSE);
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lb + t2 * 32 + 8 * g + 4 * hh);
-        float pt[4];
+      for (int e = 0; e < 16; e += 2) {
+        float pt[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pt[i] = __builtin_amdgcn_exp2f(fmaf(x[t2][4 * g + i], cs, -lse4[i]));
-        if (edge) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int qi = qrow0 + t2 * 32 + 8 * g + 4 * hh + i;
-            bool keep = qi < N;
-            if constexpr (CAUSAL) keep = keep && qi >= my_k;
-            pt[i] = keep ? pt[i] : 0.0f;
-          }
+        for (int i = 0; i < 2; ++i) {
+          pt[i] = __builtin_amdgcn_exp2f(fmaf(x[t2][e + i], cs, -lb[brow(t2, e + i)]));
+          if (CAUSAL && row0_of(0) + brow(t2, e + i) < my_k) pt[i] = 0.0f;
         }
-        w[t2][g / 2][2 * (g % 2)] = pack2<DT>(pt[0], pt[1]);
-        w[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(pt[2], pt[3]);
+        w[t2][e / 8][(e % 8) / 2] = pack2<DT>(pt[0], pt[1]);
       }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<u32x4*>(px + (c * kWave + lane) * 16) =
-          u32x4{w[c / 2][c % 2][0], w[c / 2][c % 2][1], w[c / 2][c % 2][2], w[c / 2][c % 2][3]};
+    store_b(0, w);
   };
 
-  // The 16 dwords of a P block that this lane wrote (or its partner wave's
-  // lane wrote) at px.
-  auto read_p = [&](const uint8_t* px, uint32_t (&w)[2][2][4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 pv = *reinterpret_cast<const u32x4*>(px + (c * kWave + lane) * 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[c / 2][c % 2][e] = pv[e];
-    }
-  };
-
-  // acc += (block tb)^T w: dV^T += dO^T P or dK^T += Q^T dS.
-  auto second = [&](const uint8_t* tb, const uint32_t (&w)[2][2][4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int sg = 0; sg < 2; ++sg)
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-          const u32x4 b = {w[t2][sg][0], w[t2][sg][1], w[t2][sg][2], w[t2][sg][3]};
-          acc[t] = mfma16<DT>(tr_operand<ROWB>(tb, qa, t, 2 * t2 + sg), b, acc[t]);
-        }
-    mfma_read_pipeline<4 * NDT, 2, 4>();
-  };
-
-  ld.load(qrs, q_lds[0], row0_of(0), N);
-  ld.load(qrs, q_lds[1], row0_of(1), N);
-  ld.load(dors, do_lds[0], row0_of(0), N);
-  load_d(d_lds[0], row0_of(0));
+  // Q stage 3 stands for the block before block 0 in the dK product of step
+  // 0 (against a zero dS): zero it, as uninitialised LDS may hold NaNs.
+  for (int i = tid; i < BLK / 16; i += kKVThreads)
+    reinterpret_cast<u32x4*>(smem + OFF_Q + 3 * BLK)[i] = u32x4{0u, 0u, 0u, 0u};
+  load_q(0, row0_of(0));
+  load_q(1, row0_of(1));
+  load_do(0, row0_of(0));
+  load_d(0, row0_of(0));
   load_lse(row0_of(0));
-  store_lse(lse_lds[0]);
+  store_lse(0, row0_of(0));
   load_lse(row0_of(1));
-  store_lse(lse_lds[1]);
+  store_lse(1, row0_of(1));
   bwd_barrier();
-  if (pw) p_block(0, q_lds[0], lse_lds[0], p_lds[0][grp]);
+  // Registers ra / rb: P(j) and P(j+1) of a P wave, dS(j-1) and dS(j) of a dS
+  // wave, alternating with the step's parity; dS(-1) is zero.
+  uint32_t ra[2][2][4], rb[2][2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ra[a][b][c] = rb[a][b][c] = 0u;
+  if (pw) first_p(ra);
   bwd_barrier();
 
-  // Step j; stage indices are j mod 3 (Q) and j mod 2 (the rest), fixed per
-  // unrolled copy U = j mod 6.
-  auto step = [&](int j, auto uc) __attribute__((always_inline)) {
-    constexpr int U = decltype(uc)::value;
-    constexpr int Q0 = U % 3, Q1 = (U + 1) % 3, Q2 = (U + 2) % 3, S0 = U % 2, S1 = (U + 1) % 2;
-    ld.load(qrs, q_lds[Q2], row0_of(j + 2), N);
-    ld.load(dors, do_lds[S1], row0_of(j + 1), N);
-    load_d(d_lds[S1], row0_of(j + 1));
-    load_lse(row0_of(j + 2));
-    if (pw) {
-      // dV^T += dO_j^T P_j, P_j read back from LDS; then P of block j + 1.
-      uint32_t w[2][2][4];
-      read_p(p_lds[S0][grp], w);
-      second(do_lds[S0], w);
-      __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 < nblk) p_block(j + 1, q_lds[Q1], lse_lds[S1], p_lds[S1][grp]);
-    } else {
-      // dP = dO V^T, then dS = P (dP - D) from the P wave's P, which is 0 at
-      // every masked pair.
+  // One step as a software pipeline of NM slices, like the forward's: slice m
+  // issues matrix instruction m (the 2 NKS of the first product, chain of
+  // accumulator t2 = 0 first, then the 4 NDT of the second), the LDS operand
+  // reads of instruction m + LA, and its share of the elementwise work on the
+  // first product's result: element e's first operation in slice
+  // bwd_vslice(e), once its accumulator's chain has completed, the second one
+  // slice later, the pack of a pair two slices later.  A scheduling barrier
+  // closes every slice.
+  constexpr int NS = 2 * NKS;
+  constexpr int NM = NS + 4 * NDT;
+  constexpr int LA = 4;
+  static_assert(bwd_vslice<NKS, NM>(0) - 3 >= 0 && bwd_vslice<NKS, NM>(31) + 2 <= NM,
+                "slice plan out of range");
+
+  // Each kind of wave runs its own copy of the loop (PW: the kind, a
+  // compile-time constant inside); both copies meet at the same barriers.
+  auto main_loop = [&](auto pwc) __attribute__((always_inline)) {
+    constexpr bool PW = decltype(pwc)::value;
+    auto step = [&](int j, auto uc, BRegs& r_prev, BRegs& r_cur) __attribute__((always_inline)) {
+      constexpr int U = decltype(uc)::value;
+      // Stages: Q(j+1) at (U+1)%4, Q(j-1) at (U+3)%4, Q(j+2) loads into
+      // (U+2)%4; dO(j), D(j), P(j) at U%2; LSE(j+1) at (U+1)%2.  Offsets of
+      // the stages within the A and transposed windows, and of the per-row
+      // values (LSE(j+1) log2 e or D(j)):
+      constexpr int QP = (U + 1) % 4, QD = (U + 3) % 4, QL = (U + 2) % 4;
+      constexpr int S0 = U % 2, S1 = (U + 1) % 2;
+      constexpr int AS = PW ? QP * BLK : S0 * BLK;
+      constexpr int TS = PW ? S0 * BLK : QD * BLK;
+      constexpr int RS = (PW ? S1 : S0) * kBS * 4;
+      load_q(QL, row0_of(j + 2));
+      load_do(S1, row0_of(j + 1));
+      load_d(S1, row0_of(j + 1));
+      load_lse(row0_of(j + 2));
       f32x16 x[2];
+      u32x4 opnd[LA];
+      f32x4 r4[2][4];
+      auto read = [&](auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m < NS) {
+          opnd[m % LA] = a_read(AS, m / NKS, m % NKS);
+        } else {
+          constexpr int q = m - NS, t2 = q / (2 * NDT), sg = (q / NDT) % 2, t = q % NDT;
+          opnd[m % LA] = t_read(TS, t, 2 * t2 + sg);
+        }
+      };
+      auto mfma = [&](auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m < NS) {
+          constexpr int t2 = m / NKS, ks = m % NKS;
+          x[t2] = mfma16<DT>(opnd[m % LA], kv[ks], ks == 0 ? f32x16{} : x[t2]);
+        } else {
+          constexpr int q = m - NS, t2 = q / (2 * NDT), sg = (q / NDT) % 2, t = q % NDT;
+          const u32x4 b = {r_prev[t2][sg][0], r_prev[t2][sg][1], r_prev[t2][sg][2],
+                           r_prev[t2][sg][3]};
+          acc[t] = mfma16<DT>(opnd[m % LA], b, acc[t]);
+        }
+      };
+      // P wave: P = exp2(S cs - LSE log2 e), packed into r_cur.
+      // dS wave: dS = P (dP - D), P read from r_cur, packed back into it.
+      auto elementwise = [&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) x[t2] = f32x16{};
+        for (int g = 0; g < 8; ++g)
+          if (bwd_vslice<NKS, NM>(4 * g) - 3 == k)
+            r4[g / 4][g % 4] = __builtin_bit_cast(
+                f32x4, lds16(rbase, RS + (g / 4) * 32 * 4 + 8 * (g % 4) * 4));
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+        for (int i = 0; i < 32; ++i) {
+          const int t2 = i / 16, e = i % 16, v0 = bwd_vslice<NKS, NM>(i);
+          if constexpr (PW) {
+            if (v0 == k) x[t2][e] = fmaf(x[t2][e], cs, -r4[t2][e / 4][e % 4]);
+            if (v0 + 1 == k) x[t2][e] = __builtin_amdgcn_exp2f(x[t2][e]);
+          } else {
+            if (v0 == k) x[t2][e] = x[t2][e] - r4[t2][e / 4][e % 4];
+            if (v0 + 1 == k) x[t2][e] *= elem<DT>(r_cur[t2][e / 8][(e % 8) / 2], e % 2);
+          }
+          if (i % 2 == 1 && v0 + 2 == k)
+            r_cur[t2][e / 8][(e % 8) / 2] = pack2<DT>(x[t2][e - 1], x[t2][e]);
+        }
+      };
+      static_for<0, LA>(read);
+      if constexpr (!PW) load_b(S0, r_cur);  // P(j)
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, NM + 1>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < NM) mfma(kc);
+        if constexpr (k + LA < NM) read(std::integral_constant<int, k + LA>{});
+        elementwise(kc);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr (PW) {
+        // Only S(1) of the loop's blocks can hold causally masked pairs.
+        if constexpr (CAUSAL && U == 0)
+          if (j == 0) causal_mask(r_cur, row0_of(1));
+        store_b(S1, r_cur);  // P(j+1)
+      } else {
+        // dS(j) is first used by the next step's matrix instructions: without
+        // this use here the compiler sinks its computation past the barrier,
+        // out of the slices it was meant to share.
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(r_cur[a][b][c]));
+      }
+      store_lse(S0, row0_of(j + 2));  // stage S0 held LSE(j), last used in step j-1
+      bwd_barrier();
+    };
+    // After the last step (block j), a dS wave still owes dK^T += Q(j)^T dS(j).
+    auto last = [&](auto uc, const BRegs& w) __attribute__((always_inline)) {
+      constexpr int U = decltype(uc)::value;
+      if constexpr (!PW) {
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
-          x[t2] = mfma16<DT>(row_operand<ROWB>(do_lds[S0], qa, t2, ks), kv[ks], x[t2]);
-      mfma_read_pipeline<2 * NKS, 1, 4>();
-      __builtin_amdgcn_sched_barrier(0);
-      uint32_t ds[2][2][4];
-      read_p(p_lds[S0][grp], ds);
-      const float* dlb = d_lds[S0];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+          for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlb + t2 * 32 + 8 * g + 4 * hh);
-          float v4[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            v4[i] = elem<DT>(ds[t2][g / 2][2 * (g % 2) + i / 2], i % 2) * (x[t2][4 * g + i] - d4[i]);
-          ds[t2][g / 2][2 * (g % 2)] = pack2<DT>(v4[0], v4[1]);
-          ds[t2][g / 2][2 * (g % 2) + 1] = pack2<DT>(v4[2], v4[3]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      second(q_lds[Q0], ds);
+            for (int t = 0; t < NDT; ++t) {
+              const u32x4 b = {w[t2][sg][0], w[t2][sg][1], w[t2][sg][2], w[t2][sg][3]};
+              acc[t] = mfma16<DT>(t_read((U % 4) * BLK, t, 2 * t2 + sg), b, acc[t]);
+            }
+        mfma_read_pipeline<4 * NDT, 2, 4>();
+      }
+    };
+    // Four steps per trip (stage indices fixed per copy), to the next multiple
+    // of four blocks: blocks past the last one load as zeros with LSE +inf,
+    // so their P and dS are 0 and they change neither dV nor dK.
+    for (int j = 0; j < nblk; j += 4) {
+      step(j, std::integral_constant<int, 0>{}, ra, rb);
+      step(j + 1, std::integral_constant<int, 1>{}, rb, ra);
+      step(j + 2, std::integral_constant<int, 2>{}, ra, rb);
+      step(j + 3, std::integral_constant<int, 3>{}, rb, ra);
     }
-    store_lse(lse_lds[S0]);  // LSE of block j + 2; lse_lds[S0] held block j's, used in step j - 1
-    bwd_barrier();
+    last(std::integral_constant<int, 3>{}, ra);
   };
-  for (int j = 0; j < nblk; j += 6) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 >= nblk) break;
-    step(j + 1, std::integral_constant<int, 1>{});
-    if (j + 2 >= nblk) break;
-    step(j + 2, std::integral_constant<int, 2>{});
-    if (j + 3 >= nblk) break;
-    step(j + 3, std::integral_constant<int, 3>{});
-    if (j + 4 >= nblk) break;
-    step(j + 4, std::integral_constant<int, 4>{});
-    if (j + 5 >= nblk) break;
-    step(j + 5, std::integral_constant<int, 5>{});
-  }
+  if (pw)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
 
-  // Every stage is free after the loop's last barrier: dV leaves through
-  // four of them first, then dK.
-  static_assert(kBwdWaves == 4 && BLK == kRW * D * 4, "one 32 x D fp32 block per stage");
-  uint8_t* sbuf = grp < 3 ? q_lds[grp] : do_lds[0];
+  // dV leaves through the dO and P stages (the dS waves may still read a Q
+  // stage for their last product), then dK through the Q stages.
+  static_assert(kBwdWaves == 4 && BLK == kRW * D * 4 && 2 * PSTAGE >= 2 * BLK,
+                "one 32 x D fp32 block per stage");
   const int kw0 = k0 + grp * kRW;
-  if (pw) store_rows_f32<D>(acc, 1.0f, sbuf, p.dv + head_off + (int64_t)kw0 * D, N - kw0, lane);
+  if (pw) {
+    uint8_t* sbuf = smem + (grp < 2 ? OFF_DO + grp * BLK : OFF_P + (grp - 2) * BLK);
+    store_rows_f32<D>(acc, 1.0f, sbuf, p.dv + head_off + (int64_t)kw0 * D, N - kw0, lane);
+  }
   lds_barrier();
-  if (!pw) store_rows_f32<D>(acc, p.scale, sbuf, p.dk + head_off + (int64_t)kw0 * D, N - kw0, lane);
+  if (!pw)
+    store_rows_f32<D>(acc, p.scale, smem + OFF_Q + grp * BLK,
+                      p.dk + head_off + (int64_t)kw0 * D, N - kw0, lane);
 }
 
 // ---------------------------------------------------------------------------

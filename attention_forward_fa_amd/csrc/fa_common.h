@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "fa_mi355x.h"
 
@@ -37,6 +38,15 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order (compile-time loop).
+template <int I, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
+  }
+}
 
 // Scheduling shape for a run of NM MFMAs fed by RPM LDS reads each: the reads
 // of the first LA MFMAs go first, then every MFMA is followed by the reads of

@@ -141,18 +141,6 @@ __device__ __forceinline__ f32x16 mfma_pv8(const i32x8& a, const i32x8& b, int s
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
-
-
-
-// f(integral_constant<int, I>) for I = B .. E-1, in order (compile-time loop).
-template <int I, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < E) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, E>(f);
-  }
-}
-
 // One run of NA MFMAs fed by RA LDS reads each, then NB MFMAs fed by RB
 // reads each.  The reads run LA MFMAs ahead; after every MFMA come VPM VALU
 // instructions and TPM transcendental ones (v_exp_f32 and the like form a

@@ -104,9 +104,10 @@ def test_bwd_small(dtype, d, causal, N):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("nq", range(1, 8))
 def test_bwd_every_block_count(d, nq):
-    # The dK/dV loop is unrolled six times and may leave after any copy:
-    # query block counts 1 .. 7 (N = 64 nq - 1, the last block ragged) reach
-    # every exit and the wrap back to the first copy.
+    # The dK/dV loop is unrolled four times and runs to a multiple of four
+    # blocks: query block counts 1 .. 7 (N = 64 nq - 1, the last block ragged)
+    # end on every copy, with zero to three padding blocks, once or twice
+    # round the loop.
     N = 64 * nq - 1
     inp = inputs.draw_bwd(1, 2, N, d, "fp16" if nq % 2 else "bf16", False, seed=3200 + nq + d)
     dq, dk, dv, _, _ = run_bwd(inp)
