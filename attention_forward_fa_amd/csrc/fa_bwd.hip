@@ -12,7 +12,8 @@
 //     queries, shaped like the forward: S^T = K Q^T and dP^T = V dO^T with Q
 //     and dO held in registers as B operands, dS^T in registers, then
 //     dQ^T += K^T dS^T with K^T read transposed (ds_read_b64_tr_b16) from the
-//     row-major K block in LDS.  It also computes D_i for its queries from O
+//     row-major K block in LDS; P runs beside the dP matrix instructions and
+//     dS beside the dQ ones.  It also computes D_i for its queries from O
 //     and dO and stores it (delta), for the second kernel.
 //   * fa_bwd_dkdv: one workgroup per (b, h, 128-key tile), two waves per 32
 //     keys: a P wave holds the keys' K rows, computes S = Q K^T and P per
@@ -23,8 +24,8 @@
 //     product of one block runs beside the elementwise work of the next.
 // Blocks stream global -> LDS (buffer_load ... lds, XOR-swizzled 16-byte
 // chunks), one barrier per block: the dQ kernel double-buffers K and V and
-// unrolls its loop by two (running to an even block count, the extra block
-// fully masked); the dK/dV kernel keeps four Q stages and two dO stages and
+// unrolls its loop by two (the masked blocks at the end of a wave's range
+// run one at a time); the dK/dV kernel keeps four Q stages and two dO stages and
 // unrolls by four (running to a multiple of four blocks, the extra blocks
 // zero).  Every stage index is thus a constant.  Rows past N read as zeros
 // and are masked, as are causal pairs (key j > query i).  P and dS enter the second products
@@ -235,6 +236,30 @@ __device__ __forceinline__ void bwd_barrier() {
 // ---------------------------------------------------------------------------
 // dQ (and D = rowsum(dO * O)).
 // ---------------------------------------------------------------------------
+// Slices of the dQ step.  The run is S (chain of accumulator 0, then 1),
+// dP (likewise), then dQ in four groups of NDT matrix instructions, group
+// G = (t2, sg) taking dS elements 8 sg .. 8 sg + 7 of accumulator t2.
+// dq_vp(i): slice of element i's (0 .. 31; accumulator i / 16) P: its FMA,
+// the exponential one slice later (and, in a masked block, the mask one
+// later still), once S's chain has completed.  dq_vd(i): slice of its dS:
+// the subtraction, the product one slice later, the pack of a pair two
+// slices later -- after dP's chain has completed and before its group's
+// matrix instructions.
+template <int NKS, int NDT>
+constexpr int dq_vp(int i) {
+  constexpr int NS = 2 * NKS;
+  return i < 16 ? NKS + 1 + (i * (NS - 1)) / 16 : NS + 1 + ((i - 16) * (NS - 1)) / 16;
+}
+template <int NKS, int NDT>
+constexpr int dq_vd(int i) {
+  constexpr int NS = 2 * NKS;
+  const int t2 = i / 16, e = i % 16, g = 2 * t2 + e / 8;
+  const int ready = t2 == 0 ? NS + NKS + 1 : 2 * NS + 1;
+  const int last = 2 * NS + g * NDT - 3;
+  const int first = ready > last - 4 ? ready : last - 4;
+  return first + ((e % 8) * (last - first + 1)) / 8;
+}
+
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int ROWB = D * 2;
@@ -304,69 +329,99 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
   ld.load(vrs, v_lds0, 0, kv_end);
   bwd_barrier();
 
-  auto step = [&](int j, const uint8_t* kb, const uint8_t* vb, uint8_t* kn,
-                  uint8_t* vn) __attribute__((always_inline)) {
+  // One step (key block j) as a software pipeline of NM slices: slice m
+  // issues matrix instruction m, the LDS operand reads of instruction
+  // m + LA, and its share of the elementwise work (dq_vp, dq_vd), so that
+  // P = exp2(cs S - LSE log2 e) runs beside the dP instructions and dS^T =
+  // P^T (dP^T - D) beside the dQ instructions of the group before.  A
+  // scheduling barrier closes every slice.  MASKED: the block reaches past N
+  // or, causal, past this wave's first query; its masked pairs get P = 0.
+  constexpr int NS = 2 * NKS;
+  constexpr int NM = 2 * NS + 4 * NDT;
+  constexpr int LA = 2;
+  static_assert(dq_vd<NKS, NDT>(31) + 2 < NM, "slice plan out of range");
+  auto step = [&](int j, const uint8_t* kb, const uint8_t* vb, uint8_t* kn, uint8_t* vn,
+                  auto mc) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(mc)::value;
     ld.load(krs, kn, (j + 1) * kBS, kv_end);  // next block, in flight during this one
     ld.load(vrs, vn, (j + 1) * kBS, kv_end);
-    f32x16 st[2], dpt[2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      st[t2] = f32x16{};
-      dpt[t2] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        st[t2] = mfma16<DT>(row_operand<ROWB>(kb, ka, t2, ks), qreg[ks], st[t2]);
-        dpt[t2] = mfma16<DT>(row_operand<ROWB>(vb, ka, t2, ks), doreg[ks], dpt[t2]);
-      }
-    mfma_read_pipeline<4 * NKS, 1, 2>();
-    __builtin_amdgcn_sched_barrier(0);
-    // dS^T = P^T (dP^T - D), P^T = exp2(cs s - lse log2 e); masked pairs give 0.
-    uint32_t dsw[2][2][4];
     const int kb0 = j * kBS;
-    float pt[2][16];
+    f32x16 st[2], dpt[2];
+    u32x4 opnd[LA];
+    uint32_t dsw[2][2][4];
+    auto read = [&](auto rc) __attribute__((always_inline)) {
+      constexpr int m = decltype(rc)::value;
+      if constexpr (m < 2 * NS) {
+        opnd[m % LA] = row_operand<ROWB>(m < NS ? kb : vb, ka, (m % NS) / NKS, m % NKS);
+      } else {
+        constexpr int q = m - 2 * NS, g = q / NDT, t = q % NDT;
+        opnd[m % LA] = tr_operand<ROWB>(kb, ka, t, g);
+      }
+    };
+    auto mfma = [&](auto rc) __attribute__((always_inline)) {
+      constexpr int m = decltype(rc)::value;
+      if constexpr (m < NS) {
+        constexpr int t2 = m / NKS, ks = m % NKS;
+        st[t2] = mfma16<DT>(opnd[m % LA], qreg[ks], ks == 0 ? f32x16{} : st[t2]);
+      } else if constexpr (m < 2 * NS) {
+        constexpr int t2 = (m - NS) / NKS, ks = (m - NS) % NKS;
+        dpt[t2] = mfma16<DT>(opnd[m % LA], doreg[ks], ks == 0 ? f32x16{} : dpt[t2]);
+      } else {
+        constexpr int q = m - 2 * NS, g = q / NDT, t = q % NDT;
+        const u32x4 b = {dsw[g / 2][g % 2][0], dsw[g / 2][g % 2][1], dsw[g / 2][g % 2][2],
+                         dsw[g / 2][g % 2][3]};
+        acc[t] = mfma16<DT>(opnd[m % LA], b, acc[t]);
+      }
+    };
+    auto elementwise = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pt[t2][i] = __builtin_amdgcn_exp2f(fmaf(st[t2][i], cs, -lse_l2));
-    // Only a block reaching past N or past the wave's first query needs the
-    // mask (one uniform branch; exp2 of a masked score is replaced, never used).
-    if (kb0 + kBS > N || (CAUSAL && kb0 + kBS - 1 > qw0)) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb0 + t2 * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+      for (int i = 0; i < 32; ++i) {
+        const int t2 = i / 16, e = i % 16;
+        const int vp = dq_vp<NKS, NDT>(i), vd = dq_vd<NKS, NDT>(i);
+        if (vp == k) st[t2][e] = fmaf(st[t2][e], cs, -lse_l2);
+        if (vp + 1 == k) st[t2][e] = __builtin_amdgcn_exp2f(st[t2][e]);
+        if (MASKED && vp + 2 == k) {
+          const int key = kb0 + t2 * 32 + 8 * (e / 4) + 4 * hh + (e % 4);
           bool keep = key < N;
           if constexpr (CAUSAL) keep = keep && key <= my_q;
-          pt[t2][i] = keep ? pt[t2][i] : 0.0f;
+          st[t2][e] = keep ? st[t2][e] : 0.0f;
         }
-    }
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2)
-        dsw[t2][i / 8][(i % 8) / 2] = pack2<DT>(pt[t2][i] * (dpt[t2][i] - dsum),
-                                                pt[t2][i + 1] * (dpt[t2][i + 1] - dsum));
+        if (vd == k) dpt[t2][e] -= dsum;
+        if (vd + 1 == k) dpt[t2][e] *= st[t2][e];
+        if (i % 2 == 1 && vd + 2 == k)
+          dsw[t2][e / 8][(e % 8) / 2] = pack2<DT>(dpt[t2][e - 1], dpt[t2][e]);
+      }
+    };
+    static_for<0, LA>(read);
     __builtin_amdgcn_sched_barrier(0);
-    // dQ^T += K^T dS^T.
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-          const u32x4 b = {dsw[t2][s][0], dsw[t2][s][1], dsw[t2][s][2], dsw[t2][s][3]};
-          acc[t] = mfma16<DT>(tr_operand<ROWB>(kb, ka, t, 2 * t2 + s), b, acc[t]);
-        }
-    mfma_read_pipeline<4 * NDT, 2, 2>();
+    static_for<0, NM>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      mfma(kc);
+      if constexpr (k + LA < NM) read(std::integral_constant<int, k + LA>{});
+      elementwise(kc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     bwd_barrier();
   };
-  for (int j = 0; j < nblk; j += 2) {
-    step(j, k_lds0, v_lds0, k_lds1, v_lds1);
-    step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+  // Only a block reaching past N or past the wave's first query needs the
+  // mask, and those blocks end the wave's range: blocks from j_edge on.  The
+  // loop runs the plain step in pairs (stage indices fixed per copy) below
+  // j_edge, then the masked step, stages chosen at run time, to the end.
+  // Every wave passes nblk barriers.
+  using Plain = std::false_type;
+  using Masked = std::true_type;
+  int j_edge = min(nblk, N / kBS);
+  if constexpr (CAUSAL) j_edge = min(j_edge, qw0 / kBS);
+  int j = 0;
+  for (; j + 2 <= j_edge; j += 2) {
+    step(j, k_lds0, v_lds0, k_lds1, v_lds1, Plain{});
+    step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0, Plain{});
+  }
+  for (; j < nblk; ++j) {
+    const bool odd = j & 1;
+    step(j, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
+         odd ? v_lds0 : v_lds1, Masked{});
   }
 
   // The loop's last barrier has drained every load and LDS access: the K and
