@@ -530,6 +530,13 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     kv[ks] = __builtin_amdgcn_raw_buffer_load_b128(kvrs, my_k * ROWB + (ks * 16 + 8 * hh) * 2, 0, 0);
+  // The dS wave holds -V: its product, started from D instead of zero,
+  // accumulates D - dP, and dS = P (dP - D) = (-P) (D - dP) needs no
+  // subtraction (the sign is a free source modifier of the multiply).
+  if (!pw) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kv[ks] ^= 0x80008000u;
+  }
 
   BlockAddr<ROWB> qa;
   qa.init(lane);
@@ -746,7 +753,18 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
         constexpr int m = decltype(mc)::value;
         if constexpr (m < NS) {
           constexpr int t2 = m / NKS, ks = m % NKS;
-          x[t2] = mfma16<DT>(opnd[m % LA], kv[ks], ks == 0 ? f32x16{} : x[t2]);
+          f32x16 c = x[t2];
+          if constexpr (ks == 0) {
+            if constexpr (PW) {
+              c = f32x16{};
+            } else {
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) c[4 * g + i] = r4[t2][g][i];  // D of the rows
+            }
+          }
+          x[t2] = mfma16<DT>(opnd[m % LA], kv[ks], c);
         } else {
           constexpr int q = m - NS, t2 = q / (2 * NDT), sg = (q / NDT) % 2, t = q % NDT;
           const u32x4 b = {r_prev[t2][sg][0], r_prev[t2][sg][1], r_prev[t2][sg][2],
@@ -754,15 +772,25 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
           acc[t] = mfma16<DT>(opnd[m % LA], b, acc[t]);
         }
       };
+      // The per-row values of accumulator t2: four 16-byte reads.
+      auto read_r4 = [&](int t2) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          r4[t2][g] = __builtin_bit_cast(f32x4, lds16(rbase, RS + t2 * 32 * 4 + 8 * g * 4));
+      };
       // P wave: P = exp2(S cs - LSE log2 e), packed into r_cur.
-      // dS wave: dS = P (dP - D), P read from r_cur, packed back into it.
+      // dS wave: dS = (-P) (D - dP), P read from r_cur, packed back into it.
       auto elementwise = [&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
+        if constexpr (PW) {
 #pragma unroll
-        for (int g = 0; g < 8; ++g)
-          if (bwd_vslice<NKS, NM>(4 * g) - 3 == k)
-            r4[g / 4][g % 4] = __builtin_bit_cast(
-                f32x4, lds16(rbase, RS + (g / 4) * 32 * 4 + 8 * (g % 4) * 4));
+          for (int g = 0; g < 8; ++g)
+            if (bwd_vslice<NKS, NM>(4 * g) - 3 == k)
+              r4[g / 4][g % 4] = __builtin_bit_cast(
+                  f32x4, lds16(rbase, RS + (g / 4) * 32 * 4 + 8 * (g % 4) * 4));
+        } else {
+          if constexpr (k == NKS / 2) read_r4(1);  // D for accumulator 1's chain
+        }
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           const int t2 = i / 16, e = i % 16, v0 = bwd_vslice<NKS, NM>(i);
@@ -770,13 +798,13 @@ __global__ __launch_bounds__(kKVThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p)
             if (v0 == k) x[t2][e] = fmaf(x[t2][e], cs, -r4[t2][e / 4][e % 4]);
             if (v0 + 1 == k) x[t2][e] = __builtin_amdgcn_exp2f(x[t2][e]);
           } else {
-            if (v0 == k) x[t2][e] = x[t2][e] - r4[t2][e / 4][e % 4];
-            if (v0 + 1 == k) x[t2][e] *= elem<DT>(r_cur[t2][e / 8][(e % 8) / 2], e % 2);
+            if (v0 + 1 == k) x[t2][e] *= -elem<DT>(r_cur[t2][e / 8][(e % 8) / 2], e % 2);
           }
           if (i % 2 == 1 && v0 + 2 == k)
             r_cur[t2][e / 8][(e % 8) / 2] = pack2<DT>(x[t2][e - 1], x[t2][e]);
         }
       };
+      if constexpr (!PW) read_r4(0);  // D for accumulator 0's chain
       static_for<0, LA>(read);
       if constexpr (!PW) load_b(S0, r_cur);  // P(j)
       __builtin_amdgcn_sched_barrier(0);
