@@ -8,7 +8,7 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Two kernel launches, in this order on the caller's stream:
-//   * fa_bwd_dq: one workgroup per (b, h, 128-query tile), a wave per 32
+//   * fa_bwd_dq: one workgroup per (b, h, 256-query tile), a wave per 32
 //     queries, shaped like the forward: S^T = K Q^T and dP^T = V dO^T with Q
 //     and dO held in registers as B operands, dS^T in registers, then
 //     dQ^T += K^T dS^T with K^T read transposed (ds_read_b64_tr_b16) from the
@@ -47,7 +47,10 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kWave * kBwdWaves;
 constexpr int kRW = 32;                 // rows owned by one wave
-constexpr int kBT = kRW * kBwdWaves;    // rows owned by one workgroup
+constexpr int kBT = kRW * kBwdWaves;    // keys owned by one dK/dV workgroup
+constexpr int kDqWaves = 8;             // waves of a dQ workgroup, one per 32 queries
+constexpr int kDqThreads = kWave * kDqWaves;
+constexpr int kDqT = kRW * kDqWaves;    // queries owned by one dQ workgroup
 constexpr int kBS = 64;                 // rows of one streamed block
 
 struct BwdParams {
@@ -261,7 +264,7 @@ constexpr int dq_vd(int i) {
 }
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDqThreads, 1) void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int ROWB = D * 2;
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
       reinterpret_cast<const uint8_t*>(p.o + head_off), head_bytes);
   const __amdgpu_buffer_rsrc_t dors = head_rsrc(p.dout + head_off * 2, head_bytes);
 
-  const int q0 = qt * kBT;
+  const int q0 = qt * kDqT;
   const int qw0 = q0 + wave * kRW;  // first query of this wave
   const int my_q = qw0 + lr;
   const float cs = p.scale * kLog2e;
@@ -314,11 +317,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
 
   BlockAddr<ROWB> ka;
   ka.init(lane);
-  BlockLoader<ROWB> ld;
+  BlockLoader<ROWB, kDqWaves> ld;
   ld.init(wave, lane);
 
   int kv_end = N;
-  if constexpr (CAUSAL) kv_end = min(N, q0 + kBT);
+  if constexpr (CAUSAL) kv_end = min(N, q0 + kDqT);
   const int nblk = (kv_end + kBS - 1) / kBS;
 
   f32x16 acc[NDT];
@@ -425,10 +428,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
   }
 
   // The loop's last barrier has drained every load and LDS access: the K and
-  // V stages (one 32 x D fp32 block each) are free for the row-wise store.
-  static_assert(kBwdWaves == 4 && BLK == kRW * D * 4, "one 32 x D fp32 block per stage");
-  uint8_t* sbuf = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
-  store_rows_f32<D>(acc, p.scale, sbuf, p.dq + head_off + (int64_t)qw0 * D, N - qw0, lane);
+  // V stages (one 32 x D fp32 block each) are free for the row-wise store,
+  // four waves at a time.
+  static_assert(kDqWaves == 8 && BLK == kRW * D * 4, "one 32 x D fp32 block per stage");
+  const int sw = wave % 4;
+  uint8_t* sbuf = sw == 0 ? k_lds0 : sw == 1 ? k_lds1 : sw == 2 ? v_lds0 : v_lds1;
+  float* dq_rows = p.dq + head_off + (int64_t)qw0 * D;
+  if (wave < 4) store_rows_f32<D>(acc, p.scale, sbuf, dq_rows, N - qw0, lane);
+  __syncthreads();
+  if (wave >= 4) store_rows_f32<D>(acc, p.scale, sbuf, dq_rows, N - qw0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -891,14 +899,15 @@ bool aligned_b(const void* ptr, uintptr_t a) {
 
 template <int DT, int D, bool CAUSAL>
 int launch_bwd_t(BwdParams prm, hipStream_t stream) {
-  prm.n_tiles = (prm.N + kBT - 1) / kBT;
   void* args[] = {&prm};
-  const dim3 grid((unsigned)(prm.bh * prm.n_tiles));
+  prm.n_tiles = (prm.N + kDqT - 1) / kDqT;
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<DT, D, CAUSAL>),
-                                 grid, dim3(kBwdThreads), args, 0, stream);
+                                 dim3((unsigned)(prm.bh * prm.n_tiles)), dim3(kDqThreads), args,
+                                 0, stream);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL>), grid,
-                      dim3(kKVThreads), args, 0, stream);
+  prm.n_tiles = (prm.N + kBT - 1) / kBT;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<DT, D, CAUSAL>),
+                      dim3((unsigned)(prm.bh * prm.n_tiles)), dim3(kKVThreads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
