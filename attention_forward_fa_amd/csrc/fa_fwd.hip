@@ -365,12 +365,30 @@ void fa_fwd_kernel(Params p) {
     float cb = 0.0f, lf = 0.0f, inv_f = 1.0f, vp2 = 1.0f;
     int ev = 0;
   };
-  auto tile_scale = [&](int j) __attribute__((always_inline)) {
+  // The raw K and V scales of a block are loaded one block ahead, by vector
+  // loads of a uniform address: a scalar load in flight would make every LDS
+  // wait of the loop wait for it too (the two share one counter and return
+  // out of order).  Issued before the block's K and V loads, so the wait for
+  // those at the end of an iteration covers them.
+  float sk_next = 0.0f, sv_next = 0.0f;
+  const __amdgpu_buffer_rsrc_t dks = head_rsrc(
+      reinterpret_cast<const uint8_t*>(p.descale_k + (KVT ? (int64_t)bh * p.n_kvt : 0)),
+      KVT ? p.n_kvt * 4 : 0);
+  const __amdgpu_buffer_rsrc_t dvs = head_rsrc(
+      reinterpret_cast<const uint8_t*>(p.descale_v + (KVT ? (int64_t)bh * p.n_kvt : 0)),
+      KVT ? p.n_kvt * 4 : 0);
+  auto load_scales = [&](int j) __attribute__((always_inline)) {
+    if constexpr (KVT) {
+      const int off = min(j, p.n_kvt - 1) * 4;  // blocks past N: any tile's
+      sk_next = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dks, off, 0, 0));
+      sv_next = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dvs, off, 0, 0));
+    }
+  };
+  auto tile_scale = [&](float sk, float sv) __attribute__((always_inline)) {
     TileScale t;
     if constexpr (KVT) {
-      const int64_t i = (int64_t)bh * p.n_kvt + min(j, p.n_kvt - 1);  // blocks past N: any tile's
-      const uint32_t vb = __float_as_uint(p.descale_v[i]);
-      t.cb = c * p.descale_k[i];
+      const uint32_t vb = __float_as_uint(sv);
+      t.cb = c * sk;
       t.vp2 = __uint_as_float(vb & 0xff800000u);                 // 2^ev
       const float f = __uint_as_float((vb & 0x007fffffu) | 0x3f800000u);  // [1, 2)
       t.lf = __builtin_amdgcn_logf(f);
@@ -776,6 +794,7 @@ void fa_fwd_kernel(Params p) {
       reinterpret_cast<u32x4*>(v_lds1)[i] = u32x4{0u, 0u, 0u, 0u};
     }
     constexpr int NVM = K_PER_W + 4;  // global load instructions per wave per iteration
+    load_scales(kb_lo);
     load_k(kb_lo * kBC, k_lds0);
     load_k((kb_lo + 1) * kBC, k_lds1);
     load_v(kb_lo * kBC, vst);
@@ -790,7 +809,7 @@ void fa_fwd_kernel(Params p) {
     // The reference starts at the first block's max (every row has a key in
     // the first block of its range, so it is finite).
     if (needs_mask(kb_lo)) mask(sa, kb_lo * kBC);
-    ref_c = block_max(sa) * tile_scale(kb_lo).cb;
+    ref_c = block_max(sa) * tile_scale(sk_next, sv_next).cb;
     barrier();
 
     constexpr int NPV = NDT * 4;     // P V MFMAs per block
@@ -834,7 +853,9 @@ void fa_fwd_kernel(Params p) {
                     const uint8_t* v_prev, uint8_t* v_fill, f32x16* s_cur, f32x16* s_next,
                     PRegs& p_cur, const PRegs& p_prev) __attribute__((always_inline)) {
       if (needs_mask(j)) mask(s_cur, j * kBC);
-      const TileScale ts = tile_scale(j);
+      const float sk = sk_next, sv = sv_next;
+      load_scales(j + 1);
+      const TileScale ts = tile_scale(sk, sv);
       uint32_t opnd[LA][OW];                       // operand ring, slot m % LA
       auto read = [&](auto mc) __attribute__((always_inline)) {
         constexpr int m = decltype(mc)::value;
@@ -954,6 +975,7 @@ void fa_fwd_kernel(Params p) {
     for (int i = tid; i < KBUF / 16; i += kThreads)
       reinterpret_cast<u32x4*>(v_lds3)[i] = u32x4{0u, 0u, 0u, 0u};
     constexpr int NVM8 = 2 * K_PER_W;  // global load instructions per wave per iteration
+    load_scales(kb_lo);
     load_k(kb_lo * kBC, k_lds0);
     load_v8(kb_lo * kBC, v_lds0);
     load_k((kb_lo + 1) * kBC, k_lds1);
@@ -987,11 +1009,13 @@ void fa_fwd_kernel(Params p) {
   #pragma unroll
         for (int t = 0; t < NDT; ++t) acc[t] *= alpha_prev;
       }
+      const float sk = sk_next, sv = sv_next;
+      load_scales(j + 1);
       load_v8((j + 2) * kBC, v_fill);   // V(j+2)
       load_k((j + 3) * kBC, k_fill);    // K(j+3)
       pv8(v_prev, p_prev);              // P V of block j-1
       qk(k_next, s_next);               // QK^T of block j+1
-      alpha_prev = softmax8(s_cur, p_cur, resc_prev, tile_scale(j));
+      alpha_prev = softmax8(s_cur, p_cur, resc_prev, tile_scale(sk, sv));
       mfma_run_pipeline<NDT, 4, NQK, KCH, 2, VPM8, TPM8, 0, NVM8, VM08>();
       // Keep the whole run -- softmax, P V and QK^T MFMAs -- in this block:
       // the compiler would otherwise sink MFMAs past the barrier to their
