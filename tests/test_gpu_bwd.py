@@ -114,10 +114,12 @@ def test_bwd_every_block_count(d, nq):
     check_grads(inp, (dq, dk, dv))
 
 
-def test_bwd_causal_tiles_of_every_length():
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "fp16")])
+def test_bwd_causal_tiles_of_every_length(d, dtype):
     # Causal, N = 827: the 128-key tiles start at query blocks 0, 2, .., 12
-    # and run 13, 11, 9, 7, 5, 3, 1 blocks.
-    inp = inputs.draw_bwd(1, 2, 827, 128, "bf16", True, seed=3300)
+    # and run 13, 11, 9, 7, 5, 3, 1 blocks (the dK/dV loop pads each to a
+    # multiple of four); the 256-query dQ tiles end with masked blocks.
+    inp = inputs.draw_bwd(1, 2, 827, d, dtype, True, seed=3300 + d)
     dq, dk, dv, _, _ = run_bwd(inp)
     check_grads(inp, (dq, dk, dv))
 
