@@ -44,8 +44,7 @@
 
 namespace {
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdThreads = kWave * kBwdWaves;
+constexpr int kBwdWaves = 4;           // key groups of a dK/dV workgroup
 constexpr int kRW = 32;                 // rows owned by one wave
 constexpr int kBT = kRW * kBwdWaves;    // keys owned by one dK/dV workgroup
 constexpr int kDqWaves = 8;             // waves of a dQ workgroup, one per 32 queries
