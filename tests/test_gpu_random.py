@@ -1,5 +1,6 @@
 """Randomised parity: seeded draws of shape, head dimension, dtype, causality,
-layout and entry point (fa_fwd_ex, fa_fwd_fp8_pv, fa_fwd_kvsplit; fa_bwd),
+layout and entry point (fa_fwd_ex, fa_fwd_fp8_pv, fa_fwd_kvsplit,
+fa_fwd_fp8_kvtile; fa_bwd),
 every output against the CPU fp64 oracle with the bars of the other parity
 tests.  The case lists are fixed by their seeds, so a failure names a case
 that reruns exactly."""
@@ -72,6 +73,34 @@ def test_random_forward(case):
         check_e4m3_bound(inp, on, ln)
     else:
         check(inp, on, ln)
+
+
+def _kvt_cases(n=16, seed=20261204):
+    rng = np.random.default_rng(seed)
+    return [dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)),
+                 N=int(rng.choice([1, 63, 64, 65, 129, 300, 513, 1000, 1299])),
+                 d=int(rng.choice([64, 128])), causal=bool(rng.integers(2)),
+                 layout=["bhnd", "bnhd"][rng.integers(2)],
+                 pv_min_keys=int(rng.choice([-1, -1, 0, 129, 512])), seed=3500 + i)
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _kvt_cases(), ids=lambda c: (
+    f"kvtile-B{c['B']}H{c['H']}N{c['N']}d{c['d']}-{'causal' if c['causal'] else 'full'}"
+    f"-{c['layout']}-pv{c['pv_min_keys']}-s{c['seed']}"))
+def test_random_kvtile(case):
+    # fp8 with K and V scales per 64-key tile: P V in fp16 (pv_min_keys -1)
+    # against the fp8 bars, with fp8 P V for some or all tiles against the
+    # per-element e4m3 bound (which also covers the fp16-P V rows).
+    from tests.test_gpu_kvtile import check_e4m3_bound_tiles, run_kvtile
+    inp = inputs.draw(case["B"], case["H"], case["N"], case["d"], "fp8", case["causal"],
+                      seed=case["seed"], kv_tile=binding.KV_TILE)
+    announce(f"random kvtile {case}")
+    o, l = to_np(*run_kvtile(inp, pv_min_keys=case["pv_min_keys"], layout=case["layout"]), inp)
+    if case["pv_min_keys"] < 0:
+        check(inp, o, l)
+    else:
+        check_e4m3_bound_tiles(inp, o, l)
 
 
 def _bwd_cases(n=12, seed=20261203):
