@@ -929,7 +929,21 @@ void fa_fwd_kernel(Params p) {
       const bool big = __builtin_amdgcn_ballot_w64(!(ls < kRowSumCap)) != 0;
       float alpha = 1.0f;
       if (big) {
-        alpha = rescale_block(j, k_cur, s_cur, p_cur, ts);
+        // The recomputed P is moved into the registers of the block's first P
+        // by moves whose result is tied to their destination (DPP with the
+        // identity pattern).  Left to itself the register allocator gave the
+        // two paths' P different homes and the common path copied its P
+        // (16 moves per block); tied, the common path keeps 8 64-bit moves.
+        PRegs p_new;
+        alpha = rescale_block(j, k_cur, s_cur, p_new, ts);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              p_cur[kt][h][w] = __builtin_amdgcn_update_dpp(p_cur[kt][h][w], p_new[kt][h][w],
+                                                            0xE4, 0xF, 0xF, false);
       } else {
         l_run += KVT ? ls * ts.inv_f : ls;
       }
