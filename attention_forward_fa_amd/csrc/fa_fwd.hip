@@ -1084,7 +1084,8 @@ void fa_fwd_kernel(Params p) {
     constexpr int OCH = OROWB / 16;  // 16-byte chunks per row
     constexpr int OWB = kQW * OROWB;  // bytes of one wave's block
     constexpr int WPB = KBUF / OWB;  // waves per K stage
-    static_assert(WPB >= 1 && kWaves <= 4 * WPB, "O staging must fit the K stages");
+    constexpr int WPV = PV8 ? 0 : VSTAGE / OWB;  // waves per V^T stage (used past the K stages)
+    static_assert(WPB >= 1 && kWaves <= 4 * WPB + 2 * WPV, "O staging must fit the K and V stages");
     _Float16* wrows;  // row 0 of this wave's block
     int64_t wstride;  // elements between its rows
     float* wlse;      // LSE of row 0
@@ -1100,9 +1101,15 @@ void fa_fwd_kernel(Params p) {
       wlse = p.lse + (int64_t)bh * N + qw0;
     }
     barrier();
-    const int ob = wave / WPB;
-    uint8_t* obuf = (ob == 0 ? k_lds0 : ob == 1 ? k_lds1 : ob == 2 ? k_lds2 : k_lds3) +
-                    (wave % WPB) * OWB;
+    uint8_t* obuf;
+    if (wave < 4 * WPB) {
+      const int ob = wave / WPB;
+      obuf = (ob == 0 ? k_lds0 : ob == 1 ? k_lds1 : ob == 2 ? k_lds2 : k_lds3) + (wave % WPB) * OWB;
+    } else {  // fp8 with 8 waves: the K stages hold four waves' blocks, the V^T stages the rest
+      constexpr int W = WPV > 0 ? WPV : 1;
+      const int vw = wave - 4 * WPB;
+      obuf = (vw / W == 0 ? v_lds0 : v_lds1) + (vw % W) * OWB;
+    }
     const float inv = __builtin_amdgcn_rcpf(l_tot) * v_scale;  // rows >= N are not stored
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
@@ -1278,6 +1285,15 @@ int launch_t(const Params& prm, int cus, hipStream_t stream) {
     // With 256-row tiles filling at most half the CUs, 128-row tiles on all of
     // them finish sooner although one wave per SIMD runs slower than two.
     if (2 * wgs8 <= cus) return launch_all<DT, D, CAUSAL, 4>(prm, stream);
+  }
+  if constexpr (D == 128 && DT == FA_DTYPE_FP8_E4M3) {
+    // fp8 with P V in fp16 converts V to fp16 while staging it: one 8-wave
+    // workgroup per CU converts each block once for 256 rows instead of twice
+    // for two 128-row tiles (fp8 causal [1,32,16384,128]: 2048 such tiles,
+    // 1.74-1.75 -> 1.69-1.70 ms).  With fewer than two 256-row tiles per CU
+    // the 128-row tiles balance better (fp8 causal [1,4,16384,128], 256
+    // tiles: 0.28 ms, against 0.33 with 8 waves).
+    if (wgs8 >= 2 * (int64_t)cus) return launch_all<DT, D, CAUSAL, 8>(prm, stream);
   }
   if constexpr (D == 64 && DT != FA_DTYPE_FP8_E4M3 && !CAUSAL) {
     // Non-causal d = 64 with tiles of 16 or more key blocks: one 8-wave
@@ -1535,6 +1551,12 @@ int run(const void* q, const void* k, const void* v, const float* dq, const floa
     if (d == 64)
       return causal ? launch_w<F8, 64, true, 4, false, true>(prm, 0, n64, s)
                     : launch_w<F8, 64, false, 4, false, true>(prm, 0, n64, s);
+    // d = 128: 8-wave workgroups on grids of at least two 256-row tiles per
+    // CU, as launch_t chooses for fp8 with per-head scales.
+    const int n256 = (int)((N + Shape<8>::br - 1) / Shape<8>::br);
+    if ((int64_t)prm.bh * n256 >= 2 * (int64_t)topo.cus)
+      return causal ? launch_w<F8, 128, true, 8, false, true>(prm, 0, n256, s)
+                    : launch_w<F8, 128, false, 8, false, true>(prm, 0, n256, s);
     return causal ? launch_w<F8, 128, true, 4, false, true>(prm, 0, n64, s)
                   : launch_w<F8, 128, false, 4, false, true>(prm, 0, n64, s);
   }

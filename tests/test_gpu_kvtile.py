@@ -107,6 +107,17 @@ def test_varied_tile_scales(d, causal):
     check_e4m3_bound_tiles(inp, o8, l8)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_eight_wave_kernel_ragged(causal):
+    # B*H*ceil(N/256) = 576 workgroups on 256 CUs: the 8-wave d=128 kernel with
+    # per-tile scales (P V in fp16), ragged last tile and last key block, tile
+    # scales varied within each head.
+    inp = _varied_tiles(2, 32, 2100, 128, causal, seed=5150)
+    rows = np.unique(np.concatenate([_sample_rows(inp.N, seed=5150), [2047, 2048, 2099]]))
+    o, l = to_np(*run_kvtile(inp), inp)
+    check(inp, o, l, heads=[0, 1, 33, 63], rows=rows)
+
+
 @pytest.mark.parametrize("N", (17, 129, 300))
 @pytest.mark.parametrize("causal", [False, True])
 def test_small_shapes_fp8_pv_within_e4m3_bound(N, causal):

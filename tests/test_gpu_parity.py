@@ -162,6 +162,18 @@ def test_eight_wave_kernel_ragged(dtype, causal):
     check(inp, o, l, heads=[0, 1, 16, 32], rows=rows)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_eight_wave_kernel_fp8_ragged(causal):
+    # fp8 with P V in fp16 takes 8-wave workgroups from two 256-row tiles per
+    # CU on: B*H*ceil(N/256) = 576 on 256 CUs (fewer CUs only lower the bar),
+    # ragged last tile and last key block.  With 8 waves the epilogue stages
+    # O of four waves through the V^T stages.
+    inp = inputs.draw(2, 32, 2100, 128, "fp8", causal, seed=32)
+    o, l = to_np(*gpu_run(inp), inp)
+    rows = np.unique(np.concatenate([_sample_rows(inp.N, seed=32), [2047, 2048, 2099]]))
+    check(inp, o, l, heads=[0, 1, 33, 63], rows=rows)
+
+
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_eight_wave_kernel_d64_ragged(dtype):
     # Non-causal d = 64 with N >= 1024 and B*H*ceil(N/256) = 200 workgroups:
