@@ -57,6 +57,18 @@ def test_bnhd_large_sampled():
     check(inp, on, ln, heads=[0, BH // 2, BH - 1], rows=np.array([0, 1, 255, 256, 2048, 4095]))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bnhd_fp8_eight_wave(causal):
+    # fp8 with P V in fp16 on a grid of 576 256-row tiles: the 8-wave kernel
+    # in both layouts, ragged last tile.
+    inp = inputs.draw(2, 32, 2100, 128, "fp8", causal, seed=2050)
+    o, l, o_ref, l_ref = _run_both(inp)
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(l.view(torch.int32), l_ref.view(torch.int32))
+    on, ln = to_np(o, l, inp)
+    check(inp, on, ln, heads=[0, 33, 63], rows=np.array([0, 1, 255, 256, 1024, 2047, 2048, 2099]))
+
+
 def test_bhnd_ex_matches_fa_fwd():
     inp = inputs.draw(1, 4, 300, 128, "bf16", True, seed=2100)
     q, k, v, _ = binding.to_device(inp)
