@@ -11,10 +11,12 @@
 // gfx950 mapping (the pages' TMA / mbarrier / WGMMA / TMEM machinery has no
 // counterpart here and is not imitated):
 //   * each wave of 64 lanes owns 32 query rows; a workgroup of 8 waves
-//     (fp16 / bf16, d = 128: one workgroup per CU) or 4 waves (d = 64, fp8:
-//     two workgroups per CU) covers BR = 256 or 128 rows of one (b, h) head,
-//     two waves per SIMD either way, and the whole K/V sequence streams past
-//     it in blocks of BC = 64 keys;
+//     (fp16 / bf16, d = 128: one workgroup per CU, two waves per SIMD) or 4
+//     waves (fp8: two workgroups per CU; d = 64: three) covers BR = 256 or
+//     128 rows of one (b, h) head, and the whole K/V sequence streams past
+//     it in blocks of BC = 64 keys (launch_t also picks 8 waves for d = 64
+//     non-causal with long tiles, and for fp8 at d = 128 with P V in fp16
+//     on grids of two or more 256-row tiles per CU);
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{f16,bf16} (or the fp8 v_mfma_scale_f32_32x32x64
 //     with unit block scales), Q held in registers as the B operand.  In the
@@ -86,12 +88,15 @@ struct QKOperand {
   uint32_t w[Elem<DT>::opnd_dwords];
 };
 
-// Waves per workgroup.  Eight (one workgroup per CU, two waves per SIMD) where
-// a block carries 32 MFMAs per wave (fp16 / bf16 at d = 128); four (two
-// workgroups per CU, which drift apart and fill each other's barrier waits)
-// where a block has fewer MFMAs per softmax instruction (d = 64, fp8).  The
-// eight-wave kernels have a four-wave twin (128-row tiles, one wave per SIMD)
-// for grids that would leave most CUs idle.
+// Waves per workgroup by default.  Eight (one workgroup per CU, two waves per
+// SIMD) where a block carries 32 MFMAs per wave (fp16 / bf16 at d = 128);
+// four (two workgroups per CU, three at d = 64, which drift apart and fill
+// each other's barrier waits) where a block has fewer MFMAs per softmax
+// instruction (d = 64, fp8).
+// The eight-wave kernels have a four-wave twin (128-row tiles, one wave per
+// SIMD) for grids that would leave most CUs idle; launch_t takes eight waves
+// for some four-wave cases (d = 64 non-causal, fp8 with P V in fp16), where
+// staging K and V once for 256 rows pays.
 template <int DT, int D>
 constexpr int default_waves() { return (D == 128 && DT != FA_DTYPE_FP8_E4M3) ? 8 : 4; }
 template <int WAVES>
