@@ -1,6 +1,6 @@
 """Randomised parity: seeded draws of shape, head dimension, dtype, causality,
 layout and entry point (fa_fwd_ex, fa_fwd_fp8_pv, fa_fwd_kvsplit,
-fa_fwd_fp8_kvtile; fa_bwd),
+fa_fwd_fp8_kvtile; fa_bwd; full-size fp8 grids on sampled rows),
 every output against the CPU fp64 oracle with the bars of the other parity
 tests.  The case lists are fixed by their seeds, so a failure names a case
 that reruns exactly."""
@@ -101,6 +101,52 @@ def test_random_kvtile(case):
         check(inp, o, l)
     else:
         check_e4m3_bound_tiles(inp, o, l)
+
+
+def _large_fp8_cases(n=8, seed=20261205):
+    """fp8 grids of at least two 256-row tiles per CU on a 256-CU MI355X:
+    fp16 P V runs the 8-wave kernel (per-head or per-tile scales)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B, H, N = int(rng.integers(1, 5)), int(rng.integers(8, 49)), int(rng.integers(1400, 4200))
+        if B * H * ((N + 255) // 256) < 512 or B * H * N > 2_000_000:
+            continue
+        out.append(dict(B=B, H=H, N=N, causal=bool(rng.integers(2)),
+                        layout=["bhnd", "bnhd"][rng.integers(2)],
+                        kvtile=bool(rng.integers(2)), seed=3700 + len(out)))
+    return out
+
+
+@pytest.mark.parametrize("case", _large_fp8_cases(), ids=lambda c: (
+    f"fp8large-{'kvtile' if c['kvtile'] else 'head'}-B{c['B']}H{c['H']}N{c['N']}"
+    f"-{'causal' if c['causal'] else 'full'}-{c['layout']}-s{c['seed']}"))
+def test_random_large_fp8(case):
+    # Full-size grids, oracle on sampled heads and rows (every row would take
+    # the fp64 oracle minutes).
+    from tests.test_gpu_parity import _sample_rows
+    from tests.test_gpu_kvtile import run_kvtile
+    inp = inputs.draw(case["B"], case["H"], case["N"], 128, "fp8", case["causal"],
+                      seed=case["seed"], **({"kv_tile": binding.KV_TILE} if case["kvtile"] else {}))
+    announce(f"random large fp8 {case}")
+    if case["kvtile"]:
+        o, l = run_kvtile(inp, layout=case["layout"])
+    else:
+        q, k, v, ds = binding.to_device(inp)
+        if case["layout"] == "bnhd":
+            q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+        o, l = binding.fwd_ex(q, k, v, layout=case["layout"], causal=inp.causal,
+                              scale=inp.scale, descales=ds)
+        torch.cuda.synchronize()
+        if case["layout"] == "bnhd":
+            o = o.transpose(1, 2).contiguous()
+    on, ln = to_np(o, l, inp)
+    BH = inp.B * inp.H
+    rng = np.random.default_rng(case["seed"])
+    heads = sorted({0, BH // 3, BH - 1, int(rng.integers(BH))})
+    rows = np.unique(np.concatenate([_sample_rows(inp.N, seed=case["seed"], extra=12),
+                                     [inp.N - 1]]))
+    check(inp, on, ln, heads=heads, rows=rows)
 
 
 def _bwd_cases(n=12, seed=20261203):
