@@ -11,7 +11,8 @@ harness lines ("Flash Attention CUDA Kernel 优化 ... G4", V14 to V20) agree
 with it; tests/test_accounting.py checks both against the printed numbers.
 
 Algorithmic bytes: the fused pass must read Q, K and V once and write O and
-the row log-sum-exp once; the N x N score matrix never reaches HBM.
+the row log-sum-exp once; the N x N score matrix never reaches HBM.  The
+backward likewise reads its inputs once and writes its gradients once.
 """
 from __future__ import annotations
 
@@ -33,6 +34,14 @@ def algorithmic_bytes(B: int, H: int, N: int, d: int, dtype: str) -> int:
     """Q, K, V read once + O (fp16) and LSE (fp32) written once."""
     e = ELEMENT_BYTES[dtype]
     return B * H * N * d * (3 * e + OUT_BYTES) + B * H * N * LSE_BYTES
+
+
+def algorithmic_bytes_bwd(B: int, H: int, N: int, d: int, dtype: str) -> int:
+    """Backward at the library's boundary: Q, K, V, O and dO (input type) and
+    LSE (fp32) read once; dQ, dK, dV (fp32) and delta = rowsum(dO * O)
+    (fp32) written once."""
+    e = ELEMENT_BYTES[dtype]
+    return B * H * N * d * (5 * e + 3 * 4) + B * H * N * (LSE_BYTES + 4)
 
 
 def tflops(flops: float, seconds: float) -> float:

@@ -295,28 +295,37 @@ def cpu_baseline(inp, budget_s, which="fwd"):
                       f"fp64 numpy/BLAS, {dt:.1f} s"}
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_fwd_fp16_d128_n4096_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "attention_forward_fa_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_PROFILE = {
+    "fwd": os.path.join(ROOT, "profiles", "fa_fwd_fp16_d128_n4096_traffic.txt"),
+    "bwd": os.path.join(ROOT, "profiles", "fa_bwd_fp16_d128_n4096_traffic.txt"),
+}
+KERNEL_SOURCE = {
+    "fwd": os.path.join(ROOT, "attention_forward_fa_amd", "csrc", "fa_fwd.hip"),
+    "bwd": os.path.join(ROOT, "attention_forward_fa_amd", "csrc", "fa_bwd.hip"),
+}
 
 
-def measured_traffic(workload, layout="bhnd"):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE profile, or None
-    when that profile is for another workload or an older kernel source."""
+def measured_traffic(workload, layout="bhnd", which="fwd"):
+    """HBM bytes per step (forward: its one launch; backward: the dQ and dK/dV
+    launches) from the committed FETCH_SIZE / WRITE_SIZE profile, or None when
+    that profile is for another workload or an older kernel source."""
     import hashlib
-    if workload != DEFAULT_WORKLOAD or layout != "bhnd" or not os.path.exists(TRAFFIC_PROFILE):
+    prof, src = TRAFFIC_PROFILE[which], KERNEL_SOURCE[which]
+    if workload != DEFAULT_WORKLOAD or layout != "bhnd" or not os.path.exists(prof):
         return None
     vals, sha = {}, None
-    for line in open(TRAFFIC_PROFILE, encoding="utf-8"):
+    for line in open(prof, encoding="utf-8"):
         if "source_sha256_16:" in line:
             sha = line.split("source_sha256_16:")[1].split()[0]
         elif line.strip() and not line.startswith("#"):
             k, v = line.split()[:2]
             vals[k] = float(v)
-    cur = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     if sha != cur:
         return None
-    return int(vals["fetch_kib_per_dispatch"] * 1024 * vals["fetch_scale"]
-               + vals["write_kib_per_dispatch"] * 1024 * vals["write_scale"])
+    unit = "dispatch" if which == "fwd" else "step"
+    return int(vals[f"fetch_kib_per_{unit}"] * 1024 * vals["fetch_scale"]
+               + vals[f"write_kib_per_{unit}"] * 1024 * vals["write_scale"])
 
 
 def describe(inp, sec):
@@ -381,10 +390,12 @@ def main(argv=None):
             # One step is the dQ kernel then the fused dK/dV kernel; the
             # roofline covers both (5 products counted over the step's time).
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
-                         "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                         "traffic": measured_traffic(name, "bhnd", "bwd"),
                          "scope": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel"},
             "clock": {"sclk_mhz": round(clock.mhz, 1) if clock.mhz else None,
                       "samples": len(clock.samples)},
+            "algorithmic_bytes": acc.algorithmic_bytes_bwd(B, H, N, d, dtype),
         }
         if not args.no_cpu_baseline:
             rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, "bwd")

@@ -60,3 +60,11 @@ def test_algorithmic_bytes():
     B, H, N, d = 2, 16, 4096, 128
     assert acc.algorithmic_bytes(B, H, N, d, "fp16") == B * H * N * (d * 8 + 4)
     assert acc.algorithmic_bytes(B, H, N, d, "fp8") == B * H * N * (d * 5 + 4)
+
+
+def test_algorithmic_bytes_bwd():
+    # Q, K, V, O, dO in the input type, LSE fp32 in; dQ, dK, dV and delta fp32 out.
+    B, H, N, d = 2, 16, 4096, 128
+    per_row = 5 * 2 * d + 4 + 3 * 4 * d + 4
+    assert acc.algorithmic_bytes_bwd(B, H, N, d, "fp16") == B * H * N * per_row
+    assert acc.algorithmic_bytes_bwd(B, H, N, d, "bf16") == B * H * N * (22 * d + 8)
