@@ -295,9 +295,17 @@ def cpu_baseline(inp, budget_s, which="fwd"):
                       f"fp64 numpy/BLAS, {dt:.1f} s"}
 
 
+# Committed FETCH_SIZE / WRITE_SIZE profiles: (pass, workload) -> file.  The
+# forward ones are for the plain entry point of each workload (fa_fwd_ex;
+# fa_fwd_fp8 for fp8), [B, H, N, d] layout.
 TRAFFIC_PROFILE = {
-    "fwd": os.path.join(ROOT, "profiles", "fa_fwd_fp16_d128_n4096_traffic.txt"),
-    "bwd": os.path.join(ROOT, "profiles", "fa_bwd_fp16_d128_n4096_traffic.txt"),
+    ("fwd", DEFAULT_WORKLOAD): os.path.join(ROOT, "profiles", "fa_fwd_fp16_d128_n4096_traffic.txt"),
+    ("fwd", "fp16_b4h16_n1024_d64"): os.path.join(ROOT, "profiles", "fa_fwd_fp16_d64_n1024_traffic.txt"),
+    ("fwd", "bf16_causal_b1h32_n8192_d128"):
+        os.path.join(ROOT, "profiles", "fa_fwd_bf16_causal_d128_n8192_traffic.txt"),
+    ("fwd", "fp8_causal_b1h32_n16384_d128"):
+        os.path.join(ROOT, "profiles", "fa_fwd_fp8_causal_d128_n16384_traffic.txt"),
+    ("bwd", DEFAULT_WORKLOAD): os.path.join(ROOT, "profiles", "fa_bwd_fp16_d128_n4096_traffic.txt"),
 }
 KERNEL_SOURCE = {
     "fwd": os.path.join(ROOT, "attention_forward_fa_amd", "csrc", "fa_fwd.hip"),
@@ -310,8 +318,8 @@ def measured_traffic(workload, layout="bhnd", which="fwd"):
     launches) from the committed FETCH_SIZE / WRITE_SIZE profile, or None when
     that profile is for another workload or an older kernel source."""
     import hashlib
-    prof, src = TRAFFIC_PROFILE[which], KERNEL_SOURCE[which]
-    if workload != DEFAULT_WORKLOAD or layout != "bhnd" or not os.path.exists(prof):
+    prof, src = TRAFFIC_PROFILE.get((which, workload)), KERNEL_SOURCE[which]
+    if prof is None or layout != "bhnd" or not os.path.exists(prof):
         return None
     vals, sha = {}, None
     for line in open(prof, encoding="utf-8"):
@@ -448,7 +456,9 @@ def main(argv=None):
                       if args.kv_tile else {})},
         "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tf / peak, 4),
-                     "traffic": measured_traffic(name, args.layout)},
+                     "traffic": (measured_traffic(name, args.layout)
+                                 if args.fp8_pv is None and not args.kvsplit and not args.kv_tile
+                                 else None)},
         "frac_of_peak": round(tf / peak, 4),
         # The dense peak assumes the 2400 MHz top clock; under this load the
         # package power limit holds the clock lower.  Same work, measured clock:
