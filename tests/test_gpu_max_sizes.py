@@ -104,3 +104,44 @@ def test_max_sequence_bhnd():
     torch.cuda.synchronize()
     del q, k, v
     _check(o[0], lse[0], N, [0], d, seed=32)
+
+
+def test_max_sequence_backward():
+    # fa_bwd at N = 2^22 ([1, 1, 2^22, 64] fp16, causal; dV spans 2^30 bytes
+    # of fp32).  With Q = K = 0 every P_ij is 1/(i + 1) for j <= i, dQ and dK
+    # are exactly 0 (each is a sum of terms times K or Q), and
+    # dV_j = sum_{i >= j} dO_i / (i + 1), computed here in fp64 from the end.
+    # dO[i, c] = (((29 i + 7 c) mod 13) - 6) / 16 (exact in fp16).  P enters
+    # dV rounded to fp16 (relative error <= 2^-11 each), so
+    # |dV_j - exact| <= 2^-11 sum_{i >= j} |dO_i| / (i + 1) + fp32 summation;
+    # the test allows twice the first term plus 1e-5.
+    N, d = 1 << 22, 64
+    announce(f"max sequence backward N={N} d={d} causal")
+    v = _v_pattern(N, 1, d, "bhnd")
+    q = torch.zeros_like(v)
+    k = torch.zeros_like(v)
+    i = torch.arange(N, device="cuda", dtype=torch.int32)[None, None, :, None]
+    c = torch.arange(d, device="cuda", dtype=torch.int32)[None, None, None, :]
+    do = (((29 * i + 7 * c) % 13) - 6).to(torch.float16) / 16
+    o, lse = binding.fwd(q, k, v, causal=True)
+    dq, dk, dv, _ = binding.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dq)) == 0 and int(torch.count_nonzero(dk)) == 0
+    ii = np.arange(N, dtype=np.int64)
+    w = 1.0 / (ii + 1.0)
+    rows = _rows(N, seed=33)
+    rows_t = torch.from_numpy(rows).to("cuda")
+    got = dv[0, 0].index_select(0, rows_t).double().cpu().numpy()
+    worst = 0.0
+    sums = {}  # column c depends on c only through 7 c mod 13
+    for col in range(d):
+        key = (7 * col) % 13
+        if key not in sums:
+            g = ((((29 * ii + key) % 13) - 6) / 16.0) * w
+            sums[key] = (np.cumsum(g[::-1])[::-1][rows],
+                         2.0 * 2.0 ** -11 * np.cumsum(np.abs(g)[::-1])[::-1][rows] + 1e-5)
+        exact, bound = sums[key]
+        err = np.abs(got[:, col] - exact)
+        worst = max(worst, float((err / bound).max()))
+        assert (err <= bound).all(), (col, float(err.max()), float(bound.min()))
+    announce(f"max sequence backward: max |dV - exact| / bound = {worst:.3f}")
