@@ -92,6 +92,21 @@ def test_max_head_span_bnhd():
     _check(o[0].permute(1, 0, 2), lse[0], N, [0, 7, 15], d, seed=31)
 
 
+def test_max_head_span_bnhd_fp8():
+    # fp8 e4m3 [B, N, H, d] = [1, 2^19, 16, 128] (unit descales): one head's
+    # rows span N * H * d = 2^30 bytes; a grid of 8-wave workgroups (P V in
+    # fp16), causal.  Every multiple of 1/16 up to 1/2 is an e4m3 value.
+    N, H, d = 1 << 19, 16, 128
+    announce(f"max head span bnhd fp8 N={N} H={H} d={d} causal")
+    v = _v_pattern(N, H, d, "bnhd").to(torch.float8_e4m3fn)
+    q = torch.zeros(v.shape, dtype=torch.float8_e4m3fn, device="cuda")
+    k = torch.zeros(v.shape, dtype=torch.float8_e4m3fn, device="cuda")
+    o, lse = binding.fwd_ex(q, k, v, layout="bnhd", causal=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    _check(o[0].permute(1, 0, 2), lse[0], N, [0, 9, 15], d, seed=34)
+
+
 def test_max_sequence_bhnd():
     # [B, H, N, d] = [1, 1, 2^22, 128] fp16: N at its limit, one head's rows
     # span N * d * 2 = 2^30 bytes, causal.
