@@ -15,8 +15,8 @@
 //     waves (fp8: two workgroups per CU; d = 64: three) covers BR = 256 or
 //     128 rows of one (b, h) head, and the whole K/V sequence streams past
 //     it in blocks of BC = 64 keys (launch_t also picks 8 waves for d = 64
-//     non-causal with long tiles, and for fp8 at d = 128 with P V in fp16
-//     on grids of two or more 256-row tiles per CU);
+//     with long tiles, and for fp8 at d = 128 with P V in fp16 on grids of
+//     two or more 256-row tiles per CU);
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{f16,bf16} (or the fp8 v_mfma_scale_f32_32x32x64
 //     with unit block scales), Q held in registers as the B operand.  In the
@@ -95,8 +95,8 @@ struct QKOperand {
 // instruction (d = 64, fp8).
 // The eight-wave kernels have a four-wave twin (128-row tiles, one wave per
 // SIMD) for grids that would leave most CUs idle; launch_t takes eight waves
-// for some four-wave cases (d = 64 non-causal, fp8 with P V in fp16), where
-// staging K and V once for 256 rows pays.
+// for some four-wave cases (d = 64 with long tiles, fp8 with P V in fp16),
+// where staging K and V once for 256 rows pays.
 template <int DT, int D>
 constexpr int default_waves() { return (D == 128 && DT != FA_DTYPE_FP8_E4M3) ? 8 : 4; }
 template <int WAVES>
@@ -1299,6 +1299,15 @@ int launch_t(const Params& prm, int cus, hipStream_t stream) {
     // the 128-row tiles balance better (fp8 causal [1,4,16384,128], 256
     // tiles: 0.28 ms, against 0.33 with 8 waves).
     if (wgs8 >= 2 * (int64_t)cus) return launch_all<DT, D, CAUSAL, 8>(prm, stream);
+  }
+  if constexpr (D == 64 && DT != FA_DTYPE_FP8_E4M3 && CAUSAL) {
+    // Causal d = 64 with long tiles on grids of two or more 256-row tiles per
+    // CU: 8 waves as well (fp16 [1,8,16384,64] 373 -> 337 us, [2,16,4096,64]
+    // 99.5 -> 93.3, bf16 [1,32,8192,64] 348 -> 340, [8,16,4096,64] 384 ->
+    // 381).  On fewer tiles the 4-wave workgroups balance the causal tail
+    // better ([1,16,4096,64]: 63 us, against 73 with 8 waves), and so they
+    // do for short tiles ([2,16,2048,64]: 33.6 against 41.3).
+    if (prm.N >= 4096 && wgs8 >= 2 * (int64_t)cus) return launch_all<DT, D, CAUSAL, 8>(prm, stream);
   }
   if constexpr (D == 64 && DT != FA_DTYPE_FP8_E4M3 && !CAUSAL) {
     // Non-causal d = 64 with tiles of 16 or more key blocks: one 8-wave

@@ -184,6 +184,16 @@ def test_eight_wave_kernel_d64_ragged(dtype):
     check(inp, o, l, heads=[0, 7, 21, 39], rows=rows)
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_eight_wave_kernel_d64_causal_ragged(dtype):
+    # Causal d = 64 with N >= 4096 and B*H*ceil(N/256) = 544 workgroups (two
+    # or more per CU): the 8-wave kernel at d = 64, ragged last tile.
+    inp = inputs.draw(2, 16, 4100, 64, dtype, True, seed=34)
+    o, l = to_np(*gpu_run(inp), inp)
+    rows = np.unique(np.concatenate([_sample_rows(inp.N, seed=34), [4095, 4096, 4099]]))
+    check(inp, o, l, heads=[0, 9, 22, 31], rows=rows)
+
+
 # --- edge cases and closed forms -----------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp8"])
